@@ -1,0 +1,130 @@
+/*
+ * linrec.h -- C ABI of the MI355X (gfx950) linear-recurrence scan library.
+ *
+ * The operation is the channel-wise first-order linear recurrence
+ *
+ *     h[i,0,d] = b[i,0,d]
+ *     h[i,t,d] = a[i,t,d] * h[i,t-1,d] + b[i,t,d]        t = 1 .. L-1
+ *
+ * for every batch row i < B and channel d < D, over (B, L, D) fp32 tensors with D
+ * contiguous: the problem statement of the POPCORNBENCH "Kimi-K2.6 l1_p9" and
+ * "FW-GLM-5-1 l1_p9" transcripts.  It is evaluated as an associative scan over
+ * affine pairs: applying (a1, b1) and then (a2, b2) is the pair
+ * (a2*a1, a2*b1 + b2), with identity (1, 0), and h is the second component of
+ * the inclusive scan from a zero state (the operator derivation in the first
+ * reasoning block of the Kimi-K2.6 l1_p9 transcript).  Only the running h has
+ * to cross a chunk boundary (the running-carry passage of the same block).
+ * The result is any valid bracketing of that scan in fp32 with fused
+ * multiply-add, so it is not bitwise unique; it matches a float64 sequential
+ * evaluation within 1e-4 * (1 + |h|) per element on the tested workloads.
+ *
+ * All entry points are host functions; apart from linrec_device_timeouts and
+ * linrec_release, none of them synchronises the device.
+ * No C++ or PyTorch types appear in this interface.
+ */
+#ifndef LINREC_H
+#define LINREC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum linrec_status {
+    LINREC_OK = 0,                  /* done, or enqueued on the stream                        */
+    LINREC_ERR_INVALID_ARGUMENT = 1,/* negative size, size overflow, null or non-device buffer,
+                                       buffer too small for B*L*D floats, or device mismatch   */
+    LINREC_ERR_OVERLAP = 2,         /* h overlaps a or b                                      */
+    LINREC_ERR_HIP = 3,             /* a HIP runtime call or the kernel launch failed         */
+    LINREC_ERR_OUT_OF_MEMORY = 4    /* the internal workspace could not be allocated          */
+} linrec_status;
+
+/*
+ * linrec_scan -- h = scan of the recurrence above over every (i, d) channel.
+ *
+ *   a, b   input device buffers, B*L*D fp32 each, layout (B, L, D) row-major:
+ *          element (i, t, d) at index (i*L + t)*D + d.  a[i,0,d] is never
+ *          used: the state before t = 0 is zero, so h[i,0,d] = b[i,0,d].
+ *   h      output device buffer, B*L*D fp32, same layout.  Must not overlap a
+ *          or b (a and b may alias each other).
+ *   B,L,D  sizes, each >= 0.  Any of them 0 is a successful no-op.
+ *   stream hipStream_t to enqueue on, or NULL for the null stream.
+ *
+ * Ownership: the three buffers belong to the caller and must stay valid until
+ * the work on `stream` completes; the library never frees them.  They must be
+ * device memory of the current HIP device, each inside one allocation of at
+ * least B*L*D*4 bytes (checked with the HIP runtime before launch).
+ *
+ * Workspace: when L spans several tiles the call uses a per-device workspace
+ * that the library allocates on first need (hipMalloc, outside any stream),
+ * grows when a larger shape needs more, and frees in linrec_release().  Calls
+ * on one device share it, so calls that may overlap in time on one device
+ * must be ordered on one stream; calls on different streams of one device
+ * race.  Any alignment works: 16-byte aligned buffers with D % 4 == 0 use
+ * 128-bit accesses, anything else the 32-bit form of the same kernel.
+ *
+ * Errors: returns a status and never aborts; the message for the calling
+ * thread's last failure is linrec_last_error_message().  LINREC_OK means the
+ * work is enqueued; a device fault would surface at the caller's next
+ * synchronisation.
+ *
+ * Environment: LINREC_TILE="t=<steps per lane>,w=<waves per workgroup>,vec=<1|4>"
+ * overrides the tile shape the library picks (each key optional; unsupported
+ * values are rejected with LINREC_ERR_INVALID_ARGUMENT).  LINREC_SPIN_LIMIT=<n>
+ * overrides the bound on how many times a tile polls for its predecessor's
+ * carry before giving up (see linrec_device_timeouts); it exists to exercise
+ * that path and is not a tuning knob.
+ */
+linrec_status linrec_scan(const float *a, const float *b, float *h,
+                          int64_t B, int64_t L, int64_t D, void *stream);
+
+/*
+ * linrec_plan -- how linrec_scan would run a shape: the tile it picks (after
+ * any LINREC_TILE override), the launch size and the workspace it needs.
+ */
+typedef struct linrec_plan {
+    int32_t vec;             /* channels per lane: 4 (128-bit accesses) or 1           */
+    int32_t steps_per_lane;  /* consecutive time steps each lane keeps in registers    */
+    int32_t waves;           /* 64-lane wavefronts per workgroup                       */
+    int32_t lanes_per_row;   /* lanes that share one time step of a channel slab       */
+    int64_t steps_per_tile;  /* time steps one workgroup covers                        */
+    int64_t chunks;          /* tiles along L for one (batch row, channel slab)        */
+    int64_t tiles;           /* workgroups launched (0 for an empty problem)           */
+    size_t workspace_bytes;  /* device workspace needed (0 when chunks <= 1)           */
+} linrec_plan;
+
+/*
+ * linrec_scan_plan -- fills *plan for a linrec_scan of shape (B, L, D) whose
+ * buffers are 16-byte aligned (aligned16 != 0) or not.  Pure host arithmetic,
+ * no HIP call.  Returns LINREC_ERR_INVALID_ARGUMENT for negative or
+ * overflowing sizes, an unsupported LINREC_TILE or a null plan.
+ */
+linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan *plan);
+
+/* Static English text for a status code; "unknown status" for other values. */
+const char *linrec_status_string(int status);
+
+/* Message of the calling thread's most recent failure ("" if none).  The
+ * pointer stays valid until that thread's next call into the library. */
+const char *linrec_last_error_message(void);
+
+/*
+ * linrec_device_timeouts -- number of tiles, on the current device, whose
+ * wait for a predecessor's carry exceeded the kernel's spin limit since the
+ * workspace was allocated (their outputs were written as NaN).  Synchronises
+ * the device before reading.  Returns LINREC_OK and stores the count in
+ * *count (0 when no workspace exists).
+ */
+linrec_status linrec_device_timeouts(uint64_t *count);
+
+/* Frees the per-device workspaces.  The caller must make sure no enqueued
+ * linrec_scan is still running on any device. */
+void linrec_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINREC_H */

@@ -1,0 +1,422 @@
+// linrec.hip -- host side of the C ABI in include/linrec.h: argument checks,
+// tile choice, the per-device lookback workspace and the kernel launch.
+//
+// The operation and its evaluation order are described in scan_kernel.hpp and
+// in the header; this file holds no arithmetic of the recurrence.
+#include "linrec.h"
+#include "scan_kernel.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+
+namespace {
+
+using linrec::Geometry;
+using linrec::WorkspaceHeader;
+
+thread_local std::string t_last_error;
+
+linrec_status fail(linrec_status s, const std::string& msg) {
+    t_last_error = msg;
+    return s;
+}
+
+std::string hip_text(hipError_t e) { return std::string(hipGetErrorName(e)) + ": " + hipGetErrorString(e); }
+
+// ----------------------------------------------------------------------------- tile shapes
+
+struct TileShape {
+    int vec;  // channels per lane
+    int t;    // steps per lane
+    int w;    // waves per workgroup
+};
+
+bool tile_supported(const TileShape& s) {
+    const bool vec_ok = s.vec == 1 || s.vec == 4;
+    const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
+    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8 || s.w == 16;
+    // 16 waves leave 128 registers per lane, which spills once a lane holds
+    // more than 4 steps of 4 channels
+    const bool fits = !(s.vec == 4 && s.w == 16 && s.t > 4);
+    return vec_ok && t_ok && w_ok && fits;
+}
+
+TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
+    TileShape s{vec4 ? 4 : 1, 16, 4};
+    const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
+    if (n <= 65536.0) s = TileShape{s.vec, 4, 1};
+    return s;
+}
+
+// LINREC_TILE="t=16,w=4,vec=4" (any subset of the keys).
+bool apply_tile_env(TileShape& s, std::string& err) {
+    const char* env = std::getenv("LINREC_TILE");
+    if (env == nullptr || *env == '\0') return true;
+    std::string spec(env);
+    size_t pos = 0;
+    while (pos <= spec.size()) {
+        size_t end = spec.find(',', pos);
+        if (end == std::string::npos) end = spec.size();
+        const std::string item = spec.substr(pos, end - pos);
+        const size_t eq = item.find('=');
+        if (eq == std::string::npos) {
+            err = "LINREC_TILE item '" + item + "' is not key=value";
+            return false;
+        }
+        const std::string key = item.substr(0, eq);
+        char* stop = nullptr;
+        const long val = std::strtol(item.c_str() + eq + 1, &stop, 10);
+        if (stop == item.c_str() + eq + 1 || *stop != '\0') {
+            err = "LINREC_TILE value in '" + item + "' is not an integer";
+            return false;
+        }
+        if (key == "t") s.t = static_cast<int>(val);
+        else if (key == "w") s.w = static_cast<int>(val);
+        else if (key == "vec") s.vec = static_cast<int>(val);
+        else {
+            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec";
+            return false;
+        }
+        pos = end + 1;
+    }
+    if (!tile_supported(s)) {
+        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,16}, vec in {1,4}; "
+              "vec=4 with w=16 needs t=4)";
+        return false;
+    }
+    return true;
+}
+
+uint32_t spin_limit() {
+    const char* env = std::getenv("LINREC_SPIN_LIMIT");
+    if (env != nullptr && *env != '\0') {
+        char* stop = nullptr;
+        const unsigned long v = std::strtoul(env, &stop, 10);
+        if (stop != env && *stop == '\0') return static_cast<uint32_t>(v > 0xffffffffUL ? 0xffffffffUL : v);
+    }
+    return 1u << 20;  // polls with a short sleep between them: about a second, far beyond any real wait
+}
+
+// ----------------------------------------------------------------------------- geometry
+
+struct Plan {
+    TileShape tile;
+    Geometry geom;
+    int64_t tiles;
+    size_t workspace_bytes;
+};
+
+bool checked_mul(int64_t x, int64_t y, int64_t& out) {
+    if (x == 0 || y == 0) { out = 0; return true; }
+    if (x > INT64_MAX / y) return false;
+    out = x * y;
+    return true;
+}
+
+linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p) {
+    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
+    int64_t bl = 0, n = 0;
+    if (!checked_mul(B, L, bl) || !checked_mul(bl, D, n) || n > INT64_MAX / 8)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
+
+    TileShape s = default_tile(B, L, D, aligned16 && D % 4 == 0);
+    std::string err;
+    if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
+    if (s.vec == 4 && !(aligned16 && D % 4 == 0))
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "vec=4 needs D % 4 == 0 and 16-byte aligned buffers");
+
+    p = Plan{};
+    p.tile = s;
+    Geometry& g = p.geom;
+    g.L = L;
+    g.D = D;
+    g.spin_limit = spin_limit();
+    if (n == 0) {
+        p.tiles = 0;
+        p.workspace_bytes = 0;
+        return LINREC_OK;
+    }
+    const int64_t quads = (D + s.vec - 1) / s.vec;
+    int lanes = 1, log2_lanes = 0;
+    while (lanes < linrec::kWave && lanes < quads) { lanes <<= 1; ++log2_lanes; }
+    g.lanes_d = lanes;
+    g.log2_lanes_d = log2_lanes;
+    g.groups = linrec::kWave / lanes;
+    g.slab_channels = lanes * s.vec;
+    g.nslab = static_cast<int32_t>((quads + lanes - 1) / lanes);
+    g.nseq = B * g.nslab;
+    g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
+    g.nchunks = (L + g.steps_per_tile - 1) / g.steps_per_tile;
+    int64_t tiles = 0;
+    if (!checked_mul(g.nseq, g.nchunks, tiles) || tiles * s.w * linrec::kWave > 0xffffffffLL)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more workgroups than one launch holds");
+    p.tiles = tiles;
+    g.ntiles = tiles;
+    if (g.nchunks > 1) {
+        g.nstatus = tiles * g.slab_channels;
+        p.workspace_bytes = sizeof(WorkspaceHeader) + 3 * static_cast<size_t>(g.nstatus) * sizeof(uint64_t);
+    } else {
+        g.nstatus = 0;
+        p.workspace_bytes = 0;
+    }
+    return LINREC_OK;
+}
+
+// ----------------------------------------------------------------------------- launch table
+
+using LaunchFn = void (*)(const float*, const float*, float*, const Geometry&, int64_t, WorkspaceHeader*,
+                          uint64_t*, hipStream_t);
+
+template <int VEC, int T, int W>
+void launch_tiles(const float* a, const float* b, float* h, const Geometry& g, int64_t tiles, WorkspaceHeader* hdr,
+                  uint64_t* stat, hipStream_t stream) {
+    hipLaunchKernelGGL((linrec::scan_tiles<VEC, T, W>), dim3(static_cast<uint32_t>(tiles)), dim3(W * linrec::kWave),
+                       0, stream, a, b, h, g, hdr, stat);
+}
+
+template <int VEC, int T>
+LaunchFn pick_w(int w) {
+    switch (w) {
+        case 1: return &launch_tiles<VEC, T, 1>;
+        case 2: return &launch_tiles<VEC, T, 2>;
+        case 4: return &launch_tiles<VEC, T, 4>;
+        case 8: return &launch_tiles<VEC, T, 8>;
+        case 16:
+            if constexpr (VEC == 4 && T > 4) return nullptr;
+            else return &launch_tiles<VEC, T, 16>;
+        default: return nullptr;
+    }
+}
+
+template <int VEC>
+LaunchFn pick_t(int t, int w) {
+    switch (t) {
+        case 4: return pick_w<VEC, 4>(w);
+        case 8: return pick_w<VEC, 8>(w);
+        case 16: return pick_w<VEC, 16>(w);
+        default: return nullptr;
+    }
+}
+
+LaunchFn pick_launch(const TileShape& s) { return s.vec == 4 ? pick_t<4>(s.t, s.w) : pick_t<1>(s.t, s.w); }
+
+// ----------------------------------------------------------------------------- workspace
+
+// The epoch in the status tags has 30 bits; clearing the workspace every 2^29
+// calls keeps a stale word from ever carrying the current epoch.
+constexpr uint64_t kClearPeriod = 1ull << 29;
+
+struct DeviceWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    uint64_t calls = 0;
+};
+
+std::mutex g_mutex;
+std::map<int, DeviceWorkspace> g_workspaces;
+
+linrec_status zero_fill(void* p, size_t bytes, hipStream_t stream) {
+    const int64_t words = static_cast<int64_t>(bytes / sizeof(uint32_t));
+    const int64_t blocks64 = (words + 255) / 256;
+    const unsigned blocks = static_cast<unsigned>(blocks64 < 4096 ? (blocks64 < 1 ? 1 : blocks64) : 4096);
+    hipLaunchKernelGGL(linrec::fill_zero_u32, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(p), words);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "workspace clear failed: " + hip_text(e));
+    return LINREC_OK;
+}
+
+// Returns the device workspace of at least `need` bytes, allocating or growing it.
+linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, void*& out) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    DeviceWorkspace& ws = g_workspaces[device];
+    if (ws.bytes < need) {
+        if (ws.ptr != nullptr) {
+            // the old workspace may still be in use by enqueued work
+            hipError_t e = hipDeviceSynchronize();
+            if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipDeviceSynchronize before growing the workspace: " + hip_text(e));
+            e = hipFree(ws.ptr);
+            ws = DeviceWorkspace{};
+            if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipFree of the old workspace: " + hip_text(e));
+        }
+        const size_t mib = size_t(1) << 20;
+        const size_t bytes = (need + need / 4 + mib - 1) / mib * mib;
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(LINREC_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) + " workspace bytes: " + hip_text(e));
+        }
+        e = hipMemset(p, 0, bytes);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return fail(LINREC_ERR_HIP, "clearing the new workspace: " + hip_text(e));
+        }
+        ws.ptr = p;
+        ws.bytes = bytes;
+        ws.calls = 0;
+    }
+    ws.calls += 1;
+    if (ws.calls % kClearPeriod == 0) {
+        const linrec_status s = zero_fill(ws.ptr, ws.bytes, stream);
+        if (s != LINREC_OK) return s;
+    }
+    out = ws.ptr;
+    return LINREC_OK;
+}
+
+// ----------------------------------------------------------------------------- argument checks
+
+linrec_status check_buffer(const void* p, size_t bytes, int device, const char* name) {
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " is not memory known to HIP (" + hip_text(e) + ")");
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " is not device memory");
+    if (attr.type == hipMemoryTypeDevice && attr.device != device)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " lives on device " + std::to_string(attr.device) +
+                                                     ", the current device is " + std::to_string(device));
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, const_cast<void*>(p));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + ": allocation range unknown (" + hip_text(e) + ")");
+    }
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
+    const uintptr_t at = reinterpret_cast<uintptr_t>(p);
+    if (at < lo || at - lo > size || size - (at - lo) < bytes)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " holds fewer than B*L*D floats");
+    return LINREC_OK;
+}
+
+bool overlaps(const void* x, const void* y, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
+    return a < b + bytes && b < a + bytes;
+}
+
+}  // namespace
+
+// ============================================================================= C ABI
+
+extern "C" {
+
+linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan* plan) {
+    if (plan == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "plan is null");
+    Plan p;
+    const linrec_status s = make_plan(B, L, D, aligned16 != 0, p);
+    if (s != LINREC_OK) return s;
+    plan->vec = p.tile.vec;
+    plan->steps_per_lane = p.tile.t;
+    plan->waves = p.tile.w;
+    plan->lanes_per_row = p.tiles ? p.geom.lanes_d : 0;
+    plan->steps_per_tile = p.tiles ? p.geom.steps_per_tile : 0;
+    plan->chunks = p.tiles ? p.geom.nchunks : 0;
+    plan->tiles = p.tiles;
+    plan->workspace_bytes = p.workspace_bytes;
+    return LINREC_OK;
+}
+
+linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D, void* stream) {
+    t_last_error.clear();
+    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
+    if (B == 0 || L == 0 || D == 0) return LINREC_OK;
+    if (a == nullptr || b == nullptr || h == nullptr)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "a, b and h must be non-null when B*L*D > 0");
+
+    const bool aligned16 = ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
+                             reinterpret_cast<uintptr_t>(h)) & 15u) == 0;
+    Plan p;
+    linrec_status s = make_plan(B, L, D, aligned16, p);
+    if (s != LINREC_OK) return s;
+    const size_t bytes = static_cast<size_t>(B * L * D) * sizeof(float);
+    if (overlaps(h, a, bytes) || overlaps(h, b, bytes))
+        return fail(LINREC_ERR_OVERLAP, "h overlaps a or b");
+
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: " + hip_text(e));
+    if ((s = check_buffer(a, bytes, device, "a")) != LINREC_OK) return s;
+    if ((s = check_buffer(b, bytes, device, "b")) != LINREC_OK) return s;
+    if ((s = check_buffer(h, bytes, device, "h")) != LINREC_OK) return s;
+
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    if (p.workspace_bytes > 0) {
+        s = acquire_workspace(device, p.workspace_bytes, hs, ws);
+        if (s != LINREC_OK) return s;
+    }
+    WorkspaceHeader* hdr = static_cast<WorkspaceHeader*>(ws);
+    uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader)) : nullptr;
+
+    const LaunchFn fn = pick_launch(p.tile);
+    if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
+    (void)hipGetLastError();
+    fn(a, b, h, p.geom, p.tiles, hdr, stat, hs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
+    return LINREC_OK;
+}
+
+const char* linrec_status_string(int status) {
+    switch (status) {
+        case LINREC_OK: return "success";
+        case LINREC_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case LINREC_ERR_OVERLAP: return "output overlaps an input";
+        case LINREC_ERR_HIP: return "HIP runtime error";
+        case LINREC_ERR_OUT_OF_MEMORY: return "out of device memory";
+        default: return "unknown status";
+    }
+}
+
+const char* linrec_last_error_message(void) { return t_last_error.c_str(); }
+
+linrec_status linrec_device_timeouts(uint64_t* count) {
+    if (count == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "count is null");
+    *count = 0;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: " + hip_text(e));
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        auto it = g_workspaces.find(device);
+        if (it != g_workspaces.end()) ptr = it->second.ptr;
+    }
+    if (ptr == nullptr) return LINREC_OK;
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipDeviceSynchronize: " + hip_text(e));
+    WorkspaceHeader hdr;
+    e = hipMemcpy(&hdr, ptr, sizeof(hdr), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "reading the workspace header: " + hip_text(e));
+    *count = hdr.timeouts;
+    return LINREC_OK;
+}
+
+void linrec_release(void) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    int current = 0;
+    const bool have_current = hipGetDevice(&current) == hipSuccess;
+    for (auto& kv : g_workspaces) {
+        if (kv.second.ptr == nullptr) continue;
+        if (hipSetDevice(kv.first) == hipSuccess) {
+            (void)hipDeviceSynchronize();
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_workspaces.clear();
+    if (have_current) (void)hipSetDevice(current);
+    (void)hipGetLastError();
+}
+
+}  // extern "C"

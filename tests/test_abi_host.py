@@ -1,0 +1,106 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and its host-side
+logic (status strings, plans, argument checks that return before any HIP call) behaves.
+No kernel runs here."""
+import ctypes
+import os
+import re
+from pathlib import Path
+
+import pytest
+
+from linear_recurrence_scan_linrec_amd import linrec as binding
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "linrec.h"
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(linrec_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert names, "no declarations parsed from include/linrec.h"
+    lib = ctypes.CDLL(str(binding.LIBRARY))
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, f"declared but not exported: {missing}"
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_status_strings():
+    assert binding.linrec_status_string(0) == "success"
+    assert binding.linrec_status_string(2) == "output overlaps an input"
+    assert binding.linrec_status_string(99) == "unknown status"
+
+
+def test_empty_problems_are_noops_without_touching_the_device():
+    for shape in ((0, 10, 10), (10, 0, 10), (10, 10, 0)):
+        assert binding.linrec_scan_raw(0, 0, 0, *shape, 0) == binding.LINREC_OK
+
+
+def test_invalid_sizes_and_null_buffers():
+    assert binding.linrec_scan_raw(0, 0, 0, -1, 4, 4, 0) == binding.LINREC_ERR_INVALID_ARGUMENT
+    assert "must be >= 0" in binding.linrec_last_error_message()
+    assert binding.linrec_scan_raw(0, 0, 0, 1, 4, 4, 0) == binding.LINREC_ERR_INVALID_ARGUMENT
+    assert "non-null" in binding.linrec_last_error_message()
+    big = 1 << 40
+    assert binding.linrec_scan_raw(64, 128, 256, big, big, 4, 0) == binding.LINREC_ERR_INVALID_ARGUMENT
+    assert "overflows" in binding.linrec_last_error_message()
+
+
+def test_overlap_is_rejected_before_any_hip_call():
+    # fake addresses: the overlap check runs before the buffers are looked up
+    base = 1 << 32
+    n = 2 * 8 * 16
+    assert binding.linrec_scan_raw(base, base + 4 * n, base + 8, 2, 8, 16, 0) == binding.LINREC_ERR_OVERLAP
+    assert binding.linrec_scan_raw(base, base + 4 * n, base + 4 * n + 4, 2, 8, 16, 0) == binding.LINREC_ERR_OVERLAP
+
+
+def test_plans_for_the_named_workloads():
+    p = binding.linrec_scan_plan(32, 4096, 256)
+    assert p["vec"] == 4 and p["lanes_per_row"] == 64
+    assert p["chunks"] * p["steps_per_tile"] >= 4096
+    assert p["tiles"] == 32 * p["chunks"]
+    p = binding.linrec_scan_plan(2, 262144, 64)
+    assert p["lanes_per_row"] == 16            # four rows of 64 channels per wave instruction
+    p = binding.linrec_scan_plan(1, 64, 8)
+    assert p["chunks"] == 1 and p["workspace_bytes"] == 0
+    p = binding.linrec_scan_plan(3, 100, 7)
+    assert p["vec"] == 1                       # D % 4 != 0 takes the 32-bit form
+    p = binding.linrec_scan_plan(3, 100, 8, aligned16=False)
+    assert p["vec"] == 1
+    p = binding.linrec_scan_plan(0, 100, 8)
+    assert p["tiles"] == 0 and p["workspace_bytes"] == 0
+
+
+def test_plan_workspace_covers_status_arrays():
+    p = binding.linrec_scan_plan(8, 16384, 1024)
+    per_entry = 3 * 8
+    entries = p["tiles"] * 64 * p["vec"]
+    assert p["workspace_bytes"] == 256 + per_entry * entries
+
+
+@pytest.fixture
+def tile_env():
+    old = os.environ.get("LINREC_TILE")
+    yield
+    if old is None:
+        os.environ.pop("LINREC_TILE", None)
+    else:
+        os.environ["LINREC_TILE"] = old
+
+
+def test_tile_override(tile_env):
+    os.environ["LINREC_TILE"] = "t=8,w=2"
+    p = binding.linrec_scan_plan(32, 4096, 256)
+    assert (p["steps_per_lane"], p["waves"], p["vec"]) == (8, 2, 4)
+    os.environ["LINREC_TILE"] = "vec=1"
+    assert binding.linrec_scan_plan(32, 4096, 256)["vec"] == 1
+    for bad in ("t=5", "w=3", "vec=2", "t=16,w=16", "x=1", "t", "t=abc"):
+        os.environ["LINREC_TILE"] = bad
+        with pytest.raises(binding.LinrecError) as err:
+            binding.linrec_scan_plan(32, 4096, 256)
+        assert err.value.status == binding.LINREC_ERR_INVALID_ARGUMENT
+    os.environ["LINREC_TILE"] = "vec=4"
+    with pytest.raises(binding.LinrecError):
+        binding.linrec_scan_plan(3, 100, 7)   # vec=4 cannot serve D % 4 != 0

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle, element by element.
+
+Bar: |h_gpu - h_ref| <= 1e-4 * (1 + |h_ref|) for every element (the acceptance rule of the
+harness the POPCORNBENCH transcripts were written for: fp32 compared with atol = rtol = 1e-4,
+as restated in the "Kimi-K2.6 l2_p1" transcript's correctness discussion).  Exact
+invariants (h == b where a == 0, L == 1) are checked bitwise.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import linrec_inputs as li  # noqa: E402
+import oracle  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def lr():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from linear_recurrence_scan_linrec_amd import linrec as binding
+    return binding
+
+
+def say(*args):
+    print(*args, flush=True)
+    sys.stdout.flush()
+
+
+def error_ratio(h_gpu, ref):
+    """max over elements of |h - ref| / (1 + |ref|), and its (i, t, d) index."""
+    h = h_gpu.detach().cpu().numpy().reshape(-1)
+    r = ref.reshape(-1)
+    worst, where = -1.0, 0
+    step = 1 << 24
+    for s in range(0, h.size, step):
+        hc = h[s:s + step].astype(np.float64)
+        rc = r[s:s + step]
+        ratio = np.abs(hc - rc) / (1.0 + np.abs(rc))
+        ratio[np.isnan(ratio)] = np.inf
+        k = int(np.argmax(ratio))
+        if ratio[k] > worst:
+            worst, where = float(ratio[k]), s + k
+    return worst, np.unravel_index(where, ref.shape) if ref.size else None
+
+
+def run_gpu(lr, a_np, b_np, stream=None):
+    a = torch.from_numpy(a_np).cuda()
+    b = torch.from_numpy(b_np).cuda()
+    h = lr.linrec_scan(a, b, stream=stream)
+    torch.cuda.synchronize()
+    return h
+
+
+def check_case(lr, a_np, b_np, label):
+    say(f"[parity] {label} shape={a_np.shape}")
+    h = run_gpu(lr, a_np, b_np)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    worst, where = error_ratio(h, ref)
+    say(f"[parity] {label}: max ratio {worst:.3e} at {where}")
+    assert worst <= TOL, f"{label}: max |h-ref|/(1+|ref|) = {worst:.3e} at {where}"
+    return worst
+
+
+# ----------------------------------------------------------------------------- small cases first
+
+def test_tiny_workload(lr):
+    w = li.WORKLOADS["tiny"]
+    for seed in w.seeds:
+        a, b = li.workload_inputs("tiny", seed)
+        check_case(lr, a, b, f"tiny seed={seed}")
+
+
+EDGE_SHAPES = [
+    (1, 1, 1), (1, 1, 8), (2, 2, 3), (1, 3, 4), (3, 63, 5), (2, 65, 8), (1, 64, 1), (4, 17, 2),
+    (2, 257, 256), (1, 1000, 3), (5, 129, 260), (1, 4097, 64), (2, 300, 1024), (1, 70, 4100),
+]
+
+
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_edge_shapes(lr, shape):
+    B, L, D = shape
+    a, b = li.make_inputs(B, L, D, seed=1000 + B * 7 + L * 3 + D)
+    check_case(lr, a, b, f"edge {shape}")
+
+
+def test_length_one_is_exact(lr):
+    a, b = li.make_inputs(3, 1, 40, seed=77)
+    a[:] = np.float32(np.inf)         # a_0 never contributes
+    h = run_gpu(lr, a, b).cpu().numpy()
+    assert np.array_equal(h, b)
+
+
+def supported_tiles():
+    out = []
+    for vec in (1, 4):
+        for t in (4, 8, 16):
+            for w in (1, 2, 4, 8, 16):
+                if vec == 4 and w == 16 and t > 4:
+                    continue
+                out.append((vec, t, w))
+    return out
+
+
+@pytest.fixture
+def tile_env():
+    old = os.environ.get("LINREC_TILE")
+    yield
+    if old is None:
+        os.environ.pop("LINREC_TILE", None)
+    else:
+        os.environ["LINREC_TILE"] = old
+
+
+@pytest.mark.parametrize("tile", supported_tiles(), ids=lambda t: f"vec{t[0]}_t{t[1]}_w{t[2]}")
+def test_every_tile_shape(lr, tile, tile_env):
+    """Each kernel instantiation on ragged shapes that span many tiles along L."""
+    vec, t, w = tile
+    os.environ["LINREC_TILE"] = f"vec={vec},t={t},w={w}"
+    for shape in ((3, 2999, 136), (2, 3001, 24), (1, 1500, 1 if vec == 1 else 4)):
+        a, b = li.make_inputs(*shape, seed=shape[1] + vec + t + w, a_lo=0.5, a_hi=1.0)
+        plan = lr.linrec_scan_plan(*shape)
+        assert (plan["vec"], plan["steps_per_lane"], plan["waves"]) == tile
+        check_case(lr, a, b, f"tile {tile} {shape} chunks={plan['chunks']}")
+
+
+def test_misaligned_buffers_take_the_scalar_form(lr):
+    B, L, D = 2, 700, 64
+    a_np, b_np = li.make_inputs(B, L, D, seed=31)
+    n = B * L * D
+    a_flat = torch.empty(n + 1, dtype=torch.float32, device="cuda")
+    b_flat = torch.empty(n + 1, dtype=torch.float32, device="cuda")
+    h_flat = torch.empty(n + 1, dtype=torch.float32, device="cuda")
+    a = a_flat[1:].view(B, L, D)
+    b = b_flat[1:].view(B, L, D)
+    h = h_flat[1:].view(B, L, D)
+    a.copy_(torch.from_numpy(a_np))
+    b.copy_(torch.from_numpy(b_np))
+    assert a.data_ptr() % 16 != 0
+    lr.linrec_scan(a, b, h)
+    torch.cuda.synchronize()
+    worst, where = error_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
+    assert worst <= TOL, (worst, where)
+
+
+def test_normal_a_at_the_pages_shape(lr):
+    """The pages draw both inputs with randn; a ~ N(0,1) has |a| > 1 and negative a."""
+    a, b = li.make_inputs(32, 4096, 256, seed=105, a_dist="normal")
+    check_case(lr, a, b, "pages shape, a~N(0,1)")
+
+
+# ----------------------------------------------------------------------------- the five workloads
+
+@pytest.mark.parametrize("name", ["tiny", "pages_shape", "long_sequence", "wide_channels", "near_unit_resets"])
+def test_named_workload_all_seeds(lr, name):
+    w = li.WORKLOADS[name]
+    for seed in w.seeds:
+        a, b = li.workload_inputs(name, seed)
+        check_case(lr, a, b, f"{name} seed={seed} ({w.describe()})")
+        del a, b
+
+
+def test_resets_give_b_exactly(lr):
+    a, b = li.workload_inputs("near_unit_resets", 5)
+    h = run_gpu(lr, a, b).cpu().numpy()
+    mask = a == 0
+    assert mask.sum() > 0
+    assert np.array_equal(h[mask], b[mask])
+
+
+def test_run_to_run(lr):
+    """Two runs agree within the bar; the chained tiles may pick different bracketings."""
+    for name in ("pages_shape", "long_sequence"):
+        a_np, b_np = li.workload_inputs(name)
+        a = torch.from_numpy(a_np).cuda()
+        b = torch.from_numpy(b_np).cuda()
+        h1 = lr.linrec_scan(a, b)
+        h2 = lr.linrec_scan(a, b)
+        torch.cuda.synchronize()
+        diff = ((h1 - h2).abs() / (1 + h1.abs())).max().item()
+        say(f"[determinism] {name}: max run-to-run ratio {diff:.3e}, bitwise equal {torch.equal(h1, h2)}")
+        assert diff <= TOL
+
+
+def test_non_default_stream(lr):
+    a_np, b_np = li.make_inputs(4, 5000, 256, seed=44)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = torch.from_numpy(a_np).cuda(non_blocking=False)
+        b = torch.from_numpy(b_np).cuda(non_blocking=False)
+        a2 = a * 1.0            # produced on s, consumed by the scan on s
+        h = lr.linrec_scan(a2, b, stream=s)
+        h2 = h * 1.0            # consumed on s after the scan
+    s.synchronize()
+    worst, where = error_ratio(h2, ref)
+    assert worst <= TOL, (worst, where)
+
+
+# ----------------------------------------------------------------------------- failure handling
+
+def test_spin_limit_zero_marks_late_tiles(lr):
+    """With the bounded wait forced to zero polls, a tile that finds its predecessor not ready
+    gives up at once: it counts a timeout and writes NaN; every kernel still exits normally and
+    every finite output is still right."""
+    a_np, b_np = li.make_inputs(2, 262144, 64, seed=9, a_lo=0.9, a_hi=1.0)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    before = lr.linrec_device_timeouts()
+    os.environ["LINREC_SPIN_LIMIT"] = "0"
+    try:
+        h = run_gpu(lr, a_np, b_np).cpu().numpy()
+    finally:
+        os.environ.pop("LINREC_SPIN_LIMIT")
+    late = lr.linrec_device_timeouts() - before
+    nan = np.isnan(h)
+    say(f"[timeouts] {late} tiles gave up, {int(nan.sum())} NaN outputs")
+    assert (late > 0) == bool(nan.any())
+    ok = ~nan
+    ratio = np.abs(h[ok].astype(np.float64) - ref[ok]) / (1 + np.abs(ref[ok]))
+    assert ratio.size == 0 or ratio.max() <= TOL
+    # the normal path is unaffected afterwards
+    h = run_gpu(lr, a_np, b_np)
+    assert error_ratio(h, ref)[0] <= TOL
+
+
+def test_bad_buffers_are_rejected(lr):
+    a = torch.zeros(2, 8, 16, device="cuda")
+    h = torch.zeros_like(a)
+    host = np.zeros((2, 8, 16), np.float32)
+    st = lr.linrec_scan_raw(host.ctypes.data, a.data_ptr(), h.data_ptr(), 2, 8, 16, 0)
+    assert st == lr.LINREC_ERR_INVALID_ARGUMENT
+    # a claimed size far beyond the allocations: refused (as too small, or as overlapping h)
+    st = lr.linrec_scan_raw(a.data_ptr(), a.data_ptr(), h.data_ptr(), 2, 8, 1 << 36, 0)
+    assert st in (lr.LINREC_ERR_INVALID_ARGUMENT, lr.LINREC_ERR_OVERLAP), lr.linrec_last_error_message()
+    with pytest.raises(ValueError):
+        lr.linrec_scan(a.double(), a)
+    with pytest.raises(ValueError):
+        lr.linrec_scan(a.transpose(1, 2), a.transpose(1, 2))
+    torch.cuda.synchronize()
