@@ -70,12 +70,14 @@ typedef enum linrec_status {
  * work is enqueued; a device fault would surface at the caller's next
  * synchronisation.
  *
- * Environment: LINREC_TILE="t=<steps per lane>,w=<waves per workgroup>,vec=<1|4>"
- * overrides the tile shape the library picks (each key optional; unsupported
- * values are rejected with LINREC_ERR_INVALID_ARGUMENT).  LINREC_SPIN_LIMIT=<n>
- * overrides the bound on how many times a tile polls for its predecessor's
- * carry before giving up (see linrec_device_timeouts); it exists to exercise
- * that path and is not a tuning knob.
+ * Environment: LINREC_TILE="t=<steps per lane>,w=<data waves per workgroup>,
+ * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>" overrides the tile shape
+ * and launch size the library picks (each key optional; unsupported values are
+ * rejected with LINREC_ERR_INVALID_ARGUMENT).
+ * LINREC_SPIN_LIMIT=<n> overrides how many times a tile polls a predecessor's
+ * status before it recomputes that predecessor's pair from a and b itself
+ * (see linrec_device_timeouts); results are the same either way, so it exists
+ * to exercise that path and is not a tuning knob.
  */
 linrec_status linrec_scan(const float *a, const float *b, float *h,
                           int64_t B, int64_t L, int64_t D, void *stream);
@@ -87,7 +89,7 @@ linrec_status linrec_scan(const float *a, const float *b, float *h,
 typedef struct linrec_plan {
     int32_t vec;             /* channels per lane: 4 (128-bit accesses) or 1           */
     int32_t steps_per_lane;  /* consecutive time steps each lane keeps in registers    */
-    int32_t waves;           /* 64-lane wavefronts per workgroup                       */
+    int32_t waves;           /* 64-lane data wavefronts per workgroup (plus carry ones) */
     int32_t lanes_per_row;   /* lanes that share one time step of a channel slab       */
     int64_t steps_per_tile;  /* time steps one workgroup covers                        */
     int64_t chunks;          /* tiles along L for one (batch row, channel slab)        */
@@ -111,11 +113,13 @@ const char *linrec_status_string(int status);
 const char *linrec_last_error_message(void);
 
 /*
- * linrec_device_timeouts -- number of tiles, on the current device, whose
- * wait for a predecessor's carry exceeded the kernel's spin limit since the
- * workspace was allocated (their outputs were written as NaN).  Synchronises
- * the device before reading.  Returns LINREC_OK and stores the count in
- * *count (0 when no workspace exists).
+ * linrec_device_timeouts -- on the current device, since the workspace was
+ * allocated: how many lookback wavefronts (at most four per workgroup per
+ * call) stopped waiting for a predecessor's published carry at least once and
+ * recomputed that predecessor's pair from the inputs instead.  The output is
+ * correct either way; the count shows how often the cross-workgroup wait ran
+ * out (normally 0).  Synchronises the device before reading.  Returns
+ * LINREC_OK and stores the count in *count (0 when no workspace exists).
  */
 linrec_status linrec_device_timeouts(uint64_t *count);
 

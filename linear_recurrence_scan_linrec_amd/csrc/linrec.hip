@@ -11,10 +11,12 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 
 namespace {
 
@@ -36,26 +38,39 @@ struct TileShape {
     int vec;  // channels per lane
     int t;    // steps per lane
     int w;    // waves per workgroup
+    int p;    // most lanes that share one time step of a channel slab (power of two <= 64)
+    int q;    // persistent workgroups per CU (0: as many as fit)
 };
 
 bool tile_supported(const TileShape& s) {
     const bool vec_ok = s.vec == 1 || s.vec == 4;
     const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
-    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8 || s.w == 16;
-    // 16 waves leave 128 registers per lane, which spills once a lane holds
-    // more than 4 steps of 4 channels
-    const bool fits = !(s.vec == 4 && s.w == 16 && s.t > 4);
-    return vec_ok && t_ok && w_ok && fits;
+    // w data waves plus the carry wave make up a workgroup
+    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8;
+    // two register buffers of 16 steps x 4 channels do not fit the registers a
+    // lane gets once the workgroup may hold up to 4 carry waves (they spill)
+    const bool fits = !(s.vec == 4 && s.t == 16);
+    const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
+    const bool q_ok = s.q >= 0 && s.q <= 64;
+    return vec_ok && t_ok && w_ok && fits && p_ok && q_ok;
 }
 
+// Tile choice, from sweeps on MI355X over the five workloads: 4 steps x 8
+// data waves with 32 lanes (512 bytes) per row segment streams best; when
+// there are few (batch row, channel slab) sequences, each carry chain is long
+// and bigger tiles (8 steps) shorten it.
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
-    TileShape s{vec4 ? 4 : 1, 16, 4};
+    const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
-    if (n <= 65536.0) s = TileShape{s.vec, 4, 1};
+    if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0};
+    TileShape s{vec, 4, 8, 32, 0};
+    const int64_t lanes = std::min<int64_t>(32, (D + vec - 1) / vec);
+    const int64_t sequences = B * ((D + vec * lanes - 1) / (vec * lanes));
+    if (sequences < 32) s.t = 8;
     return s;
 }
 
-// LINREC_TILE="t=16,w=4,vec=4" (any subset of the keys).
+// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2" (any subset of the keys).
 bool apply_tile_env(TileShape& s, std::string& err) {
     const char* env = std::getenv("LINREC_TILE");
     if (env == nullptr || *env == '\0') return true;
@@ -80,15 +95,17 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         if (key == "t") s.t = static_cast<int>(val);
         else if (key == "w") s.w = static_cast<int>(val);
         else if (key == "vec") s.vec = static_cast<int>(val);
+        else if (key == "p") s.p = static_cast<int>(val);
+        else if (key == "q") s.q = static_cast<int>(val);
         else {
-            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec";
+            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q";
             return false;
         }
         pos = end + 1;
     }
     if (!tile_supported(s)) {
-        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,16}, vec in {1,4}; "
-              "vec=4 with w=16 needs t=4)";
+        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8}, vec in {1,4}, "
+              "p a power of two <= 64, q in [0, 64]; not vec=4 with t=16)";
         return false;
     }
     return true;
@@ -101,7 +118,9 @@ uint32_t spin_limit() {
         const unsigned long v = std::strtoul(env, &stop, 10);
         if (stop != env && *stop == '\0') return static_cast<uint32_t>(v > 0xffffffffUL ? 0xffffffffUL : v);
     }
-    return 1u << 20;  // polls with a short sleep between them: about a second, far beyond any real wait
+    // polls of one predecessor (each a memory round trip plus a short sleep,
+    // about a microsecond) before its pair is recomputed from the inputs
+    return 512u;
 }
 
 // ----------------------------------------------------------------------------- geometry
@@ -145,23 +164,28 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
     }
     const int64_t quads = (D + s.vec - 1) / s.vec;
     int lanes = 1, log2_lanes = 0;
-    while (lanes < linrec::kWave && lanes < quads) { lanes <<= 1; ++log2_lanes; }
+    while (lanes < s.p && lanes < quads) { lanes <<= 1; ++log2_lanes; }
     g.lanes_d = lanes;
     g.log2_lanes_d = log2_lanes;
     g.groups = linrec::kWave / lanes;
     g.slab_channels = lanes * s.vec;
+    g.carry_waves = (g.slab_channels + linrec::kWave - 1) / linrec::kWave;
     g.nslab = static_cast<int32_t>((quads + lanes - 1) / lanes);
     g.nseq = B * g.nslab;
     g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
     g.nchunks = (L + g.steps_per_tile - 1) / g.steps_per_tile;
     int64_t tiles = 0;
-    if (!checked_mul(g.nseq, g.nchunks, tiles) || tiles * s.w * linrec::kWave > 0xffffffffLL)
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more workgroups than one launch holds");
+    if (!checked_mul(g.nseq, g.nchunks, tiles))
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more tiles than can be counted");
+    // a lane addresses its tile through a buffer descriptor with a 31-bit range
+    if (g.steps_per_tile * D * 4 > linrec::kMaxRange)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "one tile's rows span more than 2 GiB; pick a smaller tile (LINREC_TILE)");
     p.tiles = tiles;
     g.ntiles = tiles;
     if (g.nchunks > 1) {
         g.nstatus = tiles * g.slab_channels;
-        p.workspace_bytes = sizeof(WorkspaceHeader) + 3 * static_cast<size_t>(g.nstatus) * sizeof(uint64_t);
+        p.workspace_bytes = sizeof(WorkspaceHeader) + linrec::kDoneBytes +
+                            3 * static_cast<size_t>(g.nstatus) * sizeof(uint64_t);
     } else {
         g.nstatus = 0;
         p.workspace_bytes = 0;
@@ -171,26 +195,41 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
 
 // ----------------------------------------------------------------------------- launch table
 
-using LaunchFn = void (*)(const float*, const float*, float*, const Geometry&, int64_t, WorkspaceHeader*,
-                          uint64_t*, hipStream_t);
+struct Launch {
+    const void* kernel;   // identifies the instantiation (occupancy cache key)
+    int data_waves;
+    void (*run)(dim3 grid, dim3 block, const float*, const float*, float*, const Geometry&, WorkspaceHeader*,
+                uint64_t*, hipStream_t);
+    hipError_t (*occupancy)(int* groups_per_cu, int threads);
+};
 
 template <int VEC, int T, int W>
-void launch_tiles(const float* a, const float* b, float* h, const Geometry& g, int64_t tiles, WorkspaceHeader* hdr,
-                  uint64_t* stat, hipStream_t stream) {
-    hipLaunchKernelGGL((linrec::scan_tiles<VEC, T, W>), dim3(static_cast<uint32_t>(tiles)), dim3(W * linrec::kWave),
-                       0, stream, a, b, h, g, hdr, stat);
+void run_tiles(dim3 grid, dim3 block, const float* a, const float* b, float* h, const Geometry& g,
+               WorkspaceHeader* hdr, uint64_t* stat, hipStream_t stream) {
+    hipLaunchKernelGGL((linrec::scan_tiles<VEC, T, W>), grid, block, 0, stream, a, b, h, g, hdr, stat);
 }
+
+template <int VEC, int T, int W>
+hipError_t occupancy_of(int* groups_per_cu, int threads) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups_per_cu, linrec::scan_tiles<VEC, T, W>, threads, 0);
+}
+
+template <int VEC, int T, int W>
+const Launch* launch_entry() {
+    static const Launch entry{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>), W, &run_tiles<VEC, T, W>,
+                              &occupancy_of<VEC, T, W>};
+    return &entry;
+}
+
+using LaunchFn = const Launch*;
 
 template <int VEC, int T>
 LaunchFn pick_w(int w) {
     switch (w) {
-        case 1: return &launch_tiles<VEC, T, 1>;
-        case 2: return &launch_tiles<VEC, T, 2>;
-        case 4: return &launch_tiles<VEC, T, 4>;
-        case 8: return &launch_tiles<VEC, T, 8>;
-        case 16:
-            if constexpr (VEC == 4 && T > 4) return nullptr;
-            else return &launch_tiles<VEC, T, 16>;
+        case 1: return launch_entry<VEC, T, 1>();
+        case 2: return launch_entry<VEC, T, 2>();
+        case 4: return launch_entry<VEC, T, 4>();
+        case 8: return launch_entry<VEC, T, 8>();
         default: return nullptr;
     }
 }
@@ -200,12 +239,52 @@ LaunchFn pick_t(int t, int w) {
     switch (t) {
         case 4: return pick_w<VEC, 4>(w);
         case 8: return pick_w<VEC, 8>(w);
-        case 16: return pick_w<VEC, 16>(w);
+        case 16:
+            if constexpr (VEC == 4) return nullptr;
+            else return pick_w<VEC, 16>(w);
         default: return nullptr;
     }
 }
 
 LaunchFn pick_launch(const TileShape& s) { return s.vec == 4 ? pick_t<4>(s.t, s.w) : pick_t<1>(s.t, s.w); }
+
+// ----------------------------------------------------------------------------- persistent grid
+
+// Workgroups of one kernel instantiation that fit on the device at once
+// (occupancy per CU x CUs), cached per (device, instantiation).
+std::mutex g_grid_mutex;
+std::map<std::tuple<int, const void*, int>, int64_t> g_resident;
+
+linrec_status resident_groups(int device, const Launch* l, int threads, int64_t& out) {
+    std::lock_guard<std::mutex> lock(g_grid_mutex);
+    const auto key = std::make_tuple(device, l->kernel, threads);
+    auto it = g_resident.find(key);
+    if (it != g_resident.end()) {
+        out = it->second;
+        return LINREC_OK;
+    }
+    int per_cu = 0, cus = 0;
+    hipError_t e = l->occupancy(&per_cu, threads);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipOccupancyMaxActiveBlocksPerMultiprocessor: " + hip_text(e));
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipDeviceGetAttribute(CU count): " + hip_text(e));
+    // The occupancy query counts waves per CU; measured on gfx950, workgroups
+    // whose wave count is not a multiple of the 4 SIMDs do not all fit that
+    // way (a 5-wave workgroup puts 2 waves on one SIMD).  Count per SIMD
+    // instead: each workgroup needs ceil(waves / 4) slots on some SIMD.
+    hipFuncAttributes attr;
+    e = hipFuncGetAttributes(&attr, l->kernel);
+    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipFuncGetAttributes: " + hip_text(e));
+    const int vgprs = attr.numRegs > 0 ? (attr.numRegs + 7) / 8 * 8 : 512;
+    const int waves_per_simd = std::min(8, 512 / vgprs);
+    const int waves = threads / linrec::kWave;
+    const int per_simd_need = (waves + 3) / 4;
+    const int by_simd = std::max(1, waves_per_simd / per_simd_need);
+    per_cu = std::max(1, std::min(per_cu, by_simd));
+    out = static_cast<int64_t>(per_cu) * (cus < 1 ? 1 : cus);
+    g_resident[key] = out;
+    return LINREC_OK;
+}
 
 // ----------------------------------------------------------------------------- workspace
 
@@ -357,12 +436,26 @@ linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, i
         if (s != LINREC_OK) return s;
     }
     WorkspaceHeader* hdr = static_cast<WorkspaceHeader*>(ws);
-    uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader)) : nullptr;
+    uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader) +
+                                                      linrec::kDoneBytes)
+                        : nullptr;
 
     const LaunchFn fn = pick_launch(p.tile);
     if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
+    const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
+    int64_t resident = 0;
+    if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
+    // persistent workgroups: as many as fit at once (or fewer, per LINREC_TILE's
+    // q = workgroups per CU), never more than there are tiles
+    int64_t groups = resident;
+    if (p.tile.q > 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
+            groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);
+    }
+    groups = std::min<int64_t>(groups, p.tiles);
     (void)hipGetLastError();
-    fn(a, b, h, p.geom, p.tiles, hdr, stat, hs);
+    fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), a, b, h, p.geom, hdr, stat, hs);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
     return LINREC_OK;

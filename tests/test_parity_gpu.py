@@ -102,8 +102,8 @@ def supported_tiles():
     out = []
     for vec in (1, 4):
         for t in (4, 8, 16):
-            for w in (1, 2, 4, 8, 16):
-                if vec == 4 and w == 16 and t > 4:
+            for w in (1, 2, 4, 8):
+                if vec == 4 and t == 16:
                     continue
                 out.append((vec, t, w))
     return out
@@ -117,6 +117,17 @@ def tile_env():
         os.environ.pop("LINREC_TILE", None)
     else:
         os.environ["LINREC_TILE"] = old
+
+
+@pytest.mark.parametrize("p", [1, 2, 4, 8, 16, 32])
+def test_lanes_per_row(lr, p, tile_env):
+    """Narrower channel slabs (fewer lanes per row, more rows per wave instruction)."""
+    os.environ["LINREC_TILE"] = f"p={p}"
+    for shape in ((3, 2999, 136), (2, 1501, 256), (1, 777, 24)):
+        a, b = li.make_inputs(*shape, seed=shape[1] + p, a_lo=0.5, a_hi=1.0)
+        plan = lr.linrec_scan_plan(*shape)
+        assert plan["lanes_per_row"] <= p
+        check_case(lr, a, b, f"p={p} {shape} chunks={plan['chunks']}")
 
 
 @pytest.mark.parametrize("tile", supported_tiles(), ids=lambda t: f"vec{t[0]}_t{t[1]}_w{t[2]}")
@@ -206,28 +217,34 @@ def test_non_default_stream(lr):
 
 # ----------------------------------------------------------------------------- failure handling
 
-def test_spin_limit_zero_marks_late_tiles(lr):
-    """With the bounded wait forced to zero polls, a tile that finds its predecessor not ready
-    gives up at once: it counts a timeout and writes NaN; every kernel still exits normally and
-    every finite output is still right."""
-    a_np, b_np = li.make_inputs(2, 262144, 64, seed=9, a_lo=0.9, a_hi=1.0)
-    ref = oracle.linrec_oracle_f64(a_np, b_np)
-    before = lr.linrec_device_timeouts()
-    os.environ["LINREC_SPIN_LIMIT"] = "0"
-    try:
-        h = run_gpu(lr, a_np, b_np).cpu().numpy()
-    finally:
+@pytest.fixture
+def spin_env():
+    old = os.environ.get("LINREC_SPIN_LIMIT")
+    yield
+    if old is None:
+        os.environ.pop("LINREC_SPIN_LIMIT", None)
+    else:
+        os.environ["LINREC_SPIN_LIMIT"] = old
+
+
+def test_spin_limit_zero_recomputes_and_stays_exact(lr, spin_env):
+    """With the wait for a predecessor forced to zero polls, every tile that finds its predecessor's
+    status not yet published recomputes that predecessor's pair from a and b.  The output must not
+    change beyond the bar, and every kernel exits normally."""
+    for shape, lo in (((2, 8192, 64), 0.9), ((4, 2048, 256), 0.0)):
+        a_np, b_np = li.make_inputs(*shape, seed=9, a_lo=lo, a_hi=1.0)
+        ref = oracle.linrec_oracle_f64(a_np, b_np)
+        before = lr.linrec_device_timeouts()
+        os.environ["LINREC_SPIN_LIMIT"] = "0"
+        h = run_gpu(lr, a_np, b_np)
         os.environ.pop("LINREC_SPIN_LIMIT")
-    late = lr.linrec_device_timeouts() - before
-    nan = np.isnan(h)
-    say(f"[timeouts] {late} tiles gave up, {int(nan.sum())} NaN outputs")
-    assert (late > 0) == bool(nan.any())
-    ok = ~nan
-    ratio = np.abs(h[ok].astype(np.float64) - ref[ok]) / (1 + np.abs(ref[ok]))
-    assert ratio.size == 0 or ratio.max() <= TOL
-    # the normal path is unaffected afterwards
-    h = run_gpu(lr, a_np, b_np)
-    assert error_ratio(h, ref)[0] <= TOL
+        recomputed = lr.linrec_device_timeouts() - before
+        worst, where = error_ratio(h, ref)
+        say(f"[recompute] {shape}: {recomputed} tiles recomputed a predecessor; max ratio {worst:.3e}")
+        assert worst <= TOL, (worst, where)
+        # the normal path afterwards
+        h = run_gpu(lr, a_np, b_np)
+        assert error_ratio(h, ref)[0] <= TOL
 
 
 def test_bad_buffers_are_rejected(lr):
