@@ -8,7 +8,8 @@ steps do not find their data in the 256 MB Infinity Cache.  ``value`` is the
 algorithmic HBM throughput, 12 bytes per element (read a, read b, write h),
 over the wall time of exactly --steps steps bracketed by device
 synchronisation.  ``roofline.achieved`` uses the same bytes over the average
-kernel duration measured with HIP events on the launch stream.
+launch duration: HIP events on the launch stream bracket the timed launches,
+which run back to back.
 
 The CPU baseline leg times the float64 oracle on the same host arrays for a
 bounded number of seconds and checks the last GPU output against it.
@@ -38,7 +39,11 @@ KERNEL_SOURCES = [
     ROOT / "linear_recurrence_scan_linrec_amd" / "csrc" / "scan_kernel.hpp",
     ROOT / "include" / "linrec.h",
 ]
-TRAFFIC_FILE = ROOT / "profiles" / "traffic_scan_tiles_pages_shape.json"
+PROFILES = ROOT / "profiles"
+
+
+def traffic_file(workload: str) -> Path:
+    return PROFILES / f"traffic_scan_tiles_{workload}.json"
 
 
 def kernel_source_hash() -> str:
@@ -51,9 +56,10 @@ def kernel_source_hash() -> str:
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
     the current kernel source and this workload; otherwise None."""
-    if not TRAFFIC_FILE.exists():
+    path = traffic_file(workload)
+    if not path.exists():
         return None
-    rec = json.loads(TRAFFIC_FILE.read_text())
+    rec = json.loads(path.read_text())
     if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload:
         return None
     return int(rec["hbm_bytes_per_launch"])
@@ -68,7 +74,61 @@ def parse_args():
     p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibration-copy", type=int, default=0, metavar="N",
+                   help="after the timed steps, run N plain device copies of 512 MiB (known bytes) so that "
+                        "rocprofv3 FETCH_SIZE/WRITE_SIZE can be scaled against them")
+    p.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="no GPU work: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                        "WRITE_SIZE) of a run with --calibration-copy into the HBM bytes per scan launch, "
+                        "written to profiles/ for the roofline's traffic field")
     return p.parse_args()
+
+
+CALIBRATION_BYTES = 512 * 1024 * 1024
+
+
+def counters_by_kernel(path, counter):
+    import csv
+
+    out = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row["Kernel_Name"]
+            key = "scan" if "scan_tiles" in name else ("copy" if "copyBuffer" in name else None)
+            if key is not None:
+                out.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)   # KiB -> bytes
+    return out
+
+
+def traffic_from(fetch_csv, write_csv, workload):
+    """Scale the counters by what they read for a copy of known size; store and print the result."""
+    fetch = counters_by_kernel(fetch_csv, "FETCH_SIZE")
+    write = counters_by_kernel(write_csv, "WRITE_SIZE")
+    for name, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+        if "scan" not in d or "copy" not in d:
+            raise SystemExit(f"{name}: need both scan_tiles and copyBuffer dispatches in the csv")
+    f_factor = CALIBRATION_BYTES / float(np.mean(fetch["copy"]))
+    w_factor = CALIBRATION_BYTES / float(np.mean(write["copy"]))
+    read = float(np.mean(fetch["scan"])) * f_factor
+    written = float(np.mean(write["scan"])) * w_factor
+    w = li.WORKLOADS[workload]
+    algorithmic = 12 * w.elements
+    rec = {
+        "workload": workload,
+        "kernel_source_sha256": kernel_source_hash(),
+        "hbm_bytes_per_launch": int(round(read + written)),
+        "read_bytes_per_launch": int(round(read)),
+        "written_bytes_per_launch": int(round(written)),
+        "algorithmic_bytes_per_launch": algorithmic,
+        "fetch_scale": round(f_factor, 4),
+        "write_scale": round(w_factor, 4),
+        "scan_dispatches": [len(fetch["scan"]), len(write["scan"])],
+        "copy_dispatches": [len(fetch["copy"]), len(write["copy"])],
+    }
+    traffic_file(workload).write_text(json.dumps(rec, indent=1) + "\n")
+    print(json.dumps(rec))
 
 
 def cpu_baseline(a_np, b_np, h_last, seconds: float, shape):
@@ -101,10 +161,13 @@ def cpu_baseline(a_np, b_np, h_last, seconds: float, shape):
 
 def main():
     args = parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
-              "(the scan shards over batch rows and channels with no communication; see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported.  The scan would shard over "
+              "batch rows and channel slabs with no communication, or along L with one exchange of per-channel "
+              "carries; neither is built here.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -120,11 +183,11 @@ def main():
     n = a_np.size
     step_bytes = 12 * n
     sets = args.sets if args.sets > 0 else max(1, math.ceil(1.0e9 / step_bytes))
-    a0 = torch.from_numpy(a_np).cuda()
-    b0 = torch.from_numpy(b_np).cuda()
-    a_sets = [a0] + [a0.clone() for _ in range(sets - 1)]
-    b_sets = [b0] + [b0.clone() for _ in range(sets - 1)]
-    h_sets = [torch.empty_like(a0) for _ in range(sets)]
+    # each set is uploaded from host memory (no device-side copy kernels, so the
+    # calibration copies are the only copy dispatches in a counter profile)
+    a_sets = [torch.from_numpy(a_np).cuda() for _ in range(sets)]
+    b_sets = [torch.from_numpy(b_np).cuda() for _ in range(sets)]
+    h_sets = [torch.empty_like(a_sets[0]) for _ in range(sets)]
     stream = torch.cuda.current_stream()
     plan = lr.linrec_scan_plan(w.B, w.L, w.D)
 
@@ -133,23 +196,24 @@ def main():
         lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # one event pair on the launch stream brackets the timed launches, which run
+    # back to back; their average duration is the region's time over --steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(args.steps):
         k = (args.warmup + i) % sets
-        starts[i].record(stream)
         lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     last = (args.warmup + args.steps - 1) % sets
 
-    kernel_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+    launch_us = start.elapsed_time(end) * 1e3 / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
-    achieved = step_bytes / (kernel_ms.mean() * 1e-3) / 1e9
+    achieved = step_bytes / (launch_us * 1e-6) / 1e9
 
     out = {
         "metric": METRIC if args.workload == li.HEADLINE else f"achieved HBM GB/s, linrec_scan {w.describe()}",
@@ -172,12 +236,7 @@ def main():
         },
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "elements_per_s": round(n / (wall / args.steps), 1),
-        "kernel_us": {
-            "mean": round(float(kernel_ms.mean()) * 1e3, 2),
-            "p10": round(float(np.percentile(kernel_ms, 10)) * 1e3, 2),
-            "p50": round(float(np.percentile(kernel_ms, 50)) * 1e3, 2),
-            "p90": round(float(np.percentile(kernel_ms, 90)) * 1e3, 2),
-        },
+        "launch_us_mean": round(launch_us, 2),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -188,6 +247,13 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.calibration_copy:
+        src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.calibration_copy):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         h_last = h_sets[last].cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(a_np, b_np, h_last, args.cpu_seconds, (w.B, w.L, w.D))

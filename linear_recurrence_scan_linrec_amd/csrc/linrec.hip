@@ -175,8 +175,8 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
     g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
     g.nchunks = (L + g.steps_per_tile - 1) / g.steps_per_tile;
     int64_t tiles = 0;
-    if (!checked_mul(g.nseq, g.nchunks, tiles))
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more tiles than can be counted");
+    if (!checked_mul(g.nseq, g.nchunks, tiles) || tiles > 0x7fffffffLL)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more than 2^31 - 1 tiles; pick a larger tile (LINREC_TILE)");
     // a lane addresses its tile through a buffer descriptor with a 31-bit range
     if (g.steps_per_tile * D * 4 > linrec::kMaxRange)
         return fail(LINREC_ERR_INVALID_ARGUMENT, "one tile's rows span more than 2 GiB; pick a smaller tile (LINREC_TILE)");
@@ -216,8 +216,8 @@ hipError_t occupancy_of(int* groups_per_cu, int threads) {
 
 template <int VEC, int T, int W>
 const Launch* launch_entry() {
-    static const Launch entry{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>), W, &run_tiles<VEC, T, W>,
-                              &occupancy_of<VEC, T, W>};
+    static const Launch entry{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>), W,
+                              &run_tiles<VEC, T, W>, &occupancy_of<VEC, T, W>};
     return &entry;
 }
 

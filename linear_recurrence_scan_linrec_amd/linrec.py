@@ -125,7 +125,11 @@ def linrec_scan(a, b, h=None, stream=None):
           or not h.is_contiguous()):
         raise ValueError("h must be a contiguous float32 tensor shaped and placed like a")
     B, L, D = a.shape
-    with torch.cuda.device(a.device):
+    if a.device.index == torch.cuda.current_device():
+        s = torch.cuda.current_stream() if stream is None else stream
+        _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
+        return h
+    with torch.cuda.device(a.device):   # the library works on the current HIP device
         s = torch.cuda.current_stream(a.device) if stream is None else stream
         _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
     return h

@@ -102,7 +102,7 @@ def test_tile_override(tile_env):
     p = binding.linrec_scan_plan(32, 4096, 256)
     assert p["lanes_per_row"] == 8 and p["steps_per_tile"] == 8 * 4 * (64 // 8)
     for bad in ("t=5", "w=3", "w=16", "vec=2", "t=16", "x=1", "t", "t=abc", "p=3", "p=128", "p=0",
-                "q=-1", "q=65"):
+                "q=-1", "q=65", "d=1"):
         os.environ["LINREC_TILE"] = bad
         with pytest.raises(binding.LinrecError) as err:
             binding.linrec_scan_plan(32, 4096, 256)

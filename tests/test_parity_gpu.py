@@ -138,7 +138,7 @@ def test_every_tile_shape(lr, tile, tile_env):
     for shape in ((3, 2999, 136), (2, 3001, 24), (1, 1500, 1 if vec == 1 else 4)):
         a, b = li.make_inputs(*shape, seed=shape[1] + vec + t + w, a_lo=0.5, a_hi=1.0)
         plan = lr.linrec_scan_plan(*shape)
-        assert (plan["vec"], plan["steps_per_lane"], plan["waves"]) == tile
+        assert (plan["vec"], plan["steps_per_lane"], plan["waves"]) == (vec, t, w)
         check_case(lr, a, b, f"tile {tile} {shape} chunks={plan['chunks']}")
 
 
