@@ -34,10 +34,10 @@ import linrec_inputs as li  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "achieved HBM GB/s and % of peak, linrec_scan B=32 L=4096 D=256 fp32"
+# device code only: host-side edits that leave the kernel and its launch plan
+# unchanged keep a counter measurement valid
 KERNEL_SOURCES = [
-    ROOT / "linear_recurrence_scan_linrec_amd" / "csrc" / "linrec.hip",
     ROOT / "linear_recurrence_scan_linrec_amd" / "csrc" / "scan_kernel.hpp",
-    ROOT / "include" / "linrec.h",
 ]
 PROFILES = ROOT / "profiles"
 
@@ -53,14 +53,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def current_plan(workload: str) -> dict:
+    from linear_recurrence_scan_linrec_amd import linrec as lr
+
+    w = li.WORKLOADS[workload]
+    return lr.linrec_scan_plan(w.B, w.L, w.D)
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the current kernel source and this workload; otherwise None."""
+    the current kernel source, launch plan and workload; otherwise None."""
     path = traffic_file(workload)
     if not path.exists():
         return None
     rec = json.loads(path.read_text())
-    if rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload:
+    if (rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload
+            or rec.get("plan") != current_plan(workload)):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -118,6 +126,7 @@ def traffic_from(fetch_csv, write_csv, workload):
     rec = {
         "workload": workload,
         "kernel_source_sha256": kernel_source_hash(),
+        "plan": current_plan(workload),
         "hbm_bytes_per_launch": int(round(read + written)),
         "read_bytes_per_launch": int(round(read)),
         "written_bytes_per_launch": int(round(written)),

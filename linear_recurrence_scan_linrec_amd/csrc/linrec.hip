@@ -146,6 +146,7 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
         return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
 
     TileShape s = default_tile(B, L, D, aligned16 && D % 4 == 0);
+    if (!tile_supported(s)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
     std::string err;
     if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
     if (s.vec == 4 && !(aligned16 && D % 4 == 0))

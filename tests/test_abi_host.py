@@ -56,6 +56,14 @@ def test_overlap_is_rejected_before_any_hip_call():
     assert binding.linrec_scan_raw(base, base + 4 * n, base + 4 * n + 4, 2, 8, 16, 0) == binding.LINREC_ERR_OVERLAP
 
 
+def test_default_tiles_are_supported_for_many_shapes():
+    for B in (1, 2, 7, 32):
+        for L in (1, 100, 5000):
+            for D in (1, 3, 4, 64, 256, 1000, 8192):
+                binding.linrec_scan_plan(B, L, D)
+                binding.linrec_scan_plan(B, L, D, aligned16=False)
+
+
 def test_plans_for_the_named_workloads():
     p = binding.linrec_scan_plan(32, 4096, 256)
     assert p["vec"] == 4 and p["lanes_per_row"] <= 64
