@@ -71,9 +71,10 @@ typedef enum linrec_status {
  * synchronisation.
  *
  * Environment: LINREC_TILE="t=<steps per lane>,w=<data waves per workgroup>,
- * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>" overrides the tile shape
- * and launch size the library picks (each key optional; unsupported values are
- * rejected with LINREC_ERR_INVALID_ARGUMENT).
+ * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>" overrides the
+ * tile shape, the kernel (m=0: persistent workgroups that take tiles in turn;
+ * m=1: one workgroup per tile) and the launch size the library picks (each key
+ * optional; unsupported values are rejected with LINREC_ERR_INVALID_ARGUMENT).
  * LINREC_SPIN_LIMIT=<n> overrides how many times a tile polls a predecessor's
  * status before it recomputes that predecessor's pair from a and b itself
  * (see linrec_device_timeouts); results are the same either way, so it exists
@@ -93,8 +94,11 @@ typedef struct linrec_plan {
     int32_t lanes_per_row;   /* lanes that share one time step of a channel slab       */
     int64_t steps_per_tile;  /* time steps one workgroup covers                        */
     int64_t chunks;          /* tiles along L for one (batch row, channel slab)        */
-    int64_t tiles;           /* workgroups launched (0 for an empty problem)           */
+    int64_t tiles;           /* tiles of the problem (0 if empty); mode 1 launches one
+                                workgroup per tile, mode 0 at most as many as fit     */
     size_t workspace_bytes;  /* device workspace needed (0 when chunks <= 1)           */
+    int32_t mode;            /* 0: persistent workgroups take tiles in turn;
+                                1: one workgroup per tile                              */
 } linrec_plan;
 
 /*

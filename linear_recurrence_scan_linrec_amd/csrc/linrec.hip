@@ -40,37 +40,47 @@ struct TileShape {
     int w;    // waves per workgroup
     int p;    // most lanes that share one time step of a channel slab (power of two <= 64)
     int q;    // persistent workgroups per CU (0: as many as fit)
+    int m;    // 0: persistent workgroups with carry waves; 1: one tile per workgroup
 };
 
 bool tile_supported(const TileShape& s) {
     const bool vec_ok = s.vec == 1 || s.vec == 4;
     const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
     // w data waves plus the carry wave make up a workgroup
-    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8;
+    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 6 || s.w == 7 || s.w == 8 || s.w == 14 || s.w == 15;
+    const bool m_ok = s.m == 0 || s.m == 1;
     // two register buffers of 16 steps x 4 channels do not fit the registers a
     // lane gets once the workgroup may hold up to 4 carry waves (they spill)
-    const bool fits = !(s.vec == 4 && s.t == 16);
+    const bool fits = !(s.m == 0 && s.vec == 4 && s.t == 16) &&
+                      // 14 or 15 data waves leave at most 128 registers a lane
+                      !(s.w >= 14 && s.vec * s.t > 16);
     const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
     const bool q_ok = s.q >= 0 && s.q <= 64;
-    return vec_ok && t_ok && w_ok && fits && p_ok && q_ok;
+    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok;
 }
 
-// Tile choice, from sweeps on MI355X over the five workloads: 4 steps x 8
-// data waves with 32 lanes (512 bytes) per row segment streams best; when
-// there are few (batch row, channel slab) sequences, each carry chain is long
-// and bigger tiles (8 steps) shorten it.
+// Tile choice, from sweeps on MI355X over the five workloads: persistent
+// workgroups of 8 data waves, 4 steps per lane and 32 lanes (512 bytes) per
+// row segment stream best when there are many (batch row, channel slab)
+// sequences.  With few sequences each carry chain is long: one workgroup per
+// tile, 15 data waves and a single carry wave (64-channel slabs) then keep
+// more tiles in flight along each chain.
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
     const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
-    if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0};
-    TileShape s{vec, 4, 8, 32, 0};
+    if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0, 0};
+    TileShape s{vec, 4, 8, 32, 0, 0};
     const int64_t lanes = std::min<int64_t>(32, (D + vec - 1) / vec);
     const int64_t sequences = B * ((D + vec * lanes - 1) / (vec * lanes));
-    if (sequences < 32) s.t = 8;
+    if (sequences < 32) {
+        s.m = 1;
+        s.w = 15;
+        s.p = 64 / vec;
+    }
     return s;
 }
 
-// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2" (any subset of the keys).
+// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0" (any subset of the keys).
 bool apply_tile_env(TileShape& s, std::string& err) {
     const char* env = std::getenv("LINREC_TILE");
     if (env == nullptr || *env == '\0') return true;
@@ -97,15 +107,17 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         else if (key == "vec") s.vec = static_cast<int>(val);
         else if (key == "p") s.p = static_cast<int>(val);
         else if (key == "q") s.q = static_cast<int>(val);
+        else if (key == "m") s.m = static_cast<int>(val);
         else {
-            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q";
+            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q, m";
             return false;
         }
         pos = end + 1;
     }
     if (!tile_supported(s)) {
-        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8}, vec in {1,4}, "
-              "p a power of two <= 64, q in [0, 64]; not vec=4 with t=16)";
+        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,6,7,8,14,15}, vec in {1,4}, "
+              "p a power of two <= 64, q in [0, 64], m in {0,1}; not vec=4 with t=16 and m=0, "
+              "not w >= 14 with vec*t > 16)";
         return false;
     }
     return true;
@@ -171,6 +183,9 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
     g.groups = linrec::kWave / lanes;
     g.slab_channels = lanes * s.vec;
     g.carry_waves = (g.slab_channels + linrec::kWave - 1) / linrec::kWave;
+    if ((s.w + g.carry_waves) * linrec::kWave > 1024)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "the tile needs more than 1024 threads per workgroup (data waves w "
+                                                 "plus one carry wave per 64 slab channels); pick a smaller w or p");
     g.nslab = static_cast<int32_t>((quads + lanes - 1) / lanes);
     g.nseq = B * g.nslab;
     g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
@@ -198,7 +213,6 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
 
 struct Launch {
     const void* kernel;   // identifies the instantiation (occupancy cache key)
-    int data_waves;
     void (*run)(dim3 grid, dim3 block, const float*, const float*, float*, const Geometry&, WorkspaceHeader*,
                 uint64_t*, hipStream_t);
     hipError_t (*occupancy)(int* groups_per_cu, int threads);
@@ -216,38 +230,62 @@ hipError_t occupancy_of(int* groups_per_cu, int threads) {
 }
 
 template <int VEC, int T, int W>
-const Launch* launch_entry() {
-    static const Launch entry{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>), W,
-                              &run_tiles<VEC, T, W>, &occupancy_of<VEC, T, W>};
-    return &entry;
+void run_one(dim3 grid, dim3 block, const float* a, const float* b, float* h, const Geometry& g,
+             WorkspaceHeader* hdr, uint64_t* stat, hipStream_t stream) {
+    hipLaunchKernelGGL((linrec::scan_one<VEC, T, W>), grid, block, 0, stream, a, b, h, g, hdr, stat);
+}
+
+template <int VEC, int T, int W>
+hipError_t occupancy_one(int* groups_per_cu, int threads) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups_per_cu, linrec::scan_one<VEC, T, W>, threads, 0);
+}
+
+template <int VEC, int T, int W>
+const Launch* launch_entry(int mode) {
+    if (mode == 1) {
+        static const Launch one{reinterpret_cast<const void*>(&linrec::scan_one<VEC, T, W>), &run_one<VEC, T, W>,
+                                &occupancy_one<VEC, T, W>};
+        return &one;
+    }
+    if constexpr (VEC == 4 && T == 16) {
+        return nullptr;   // two such register buffers spill
+    } else {
+        static const Launch persistent{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>),
+                                       &run_tiles<VEC, T, W>, &occupancy_of<VEC, T, W>};
+        return &persistent;
+    }
 }
 
 using LaunchFn = const Launch*;
 
 template <int VEC, int T>
-LaunchFn pick_w(int w) {
+LaunchFn pick_w(int w, int m) {
     switch (w) {
-        case 1: return launch_entry<VEC, T, 1>();
-        case 2: return launch_entry<VEC, T, 2>();
-        case 4: return launch_entry<VEC, T, 4>();
-        case 8: return launch_entry<VEC, T, 8>();
+        case 1: return launch_entry<VEC, T, 1>(m);
+        case 2: return launch_entry<VEC, T, 2>(m);
+        case 4: return launch_entry<VEC, T, 4>(m);
+        case 6: return launch_entry<VEC, T, 6>(m);
+        case 7: return launch_entry<VEC, T, 7>(m);
+        case 8: return launch_entry<VEC, T, 8>(m);
+        case 14: return launch_entry<VEC, T, 14>(m);
+        case 15: return launch_entry<VEC, T, 15>(m);
         default: return nullptr;
     }
 }
 
 template <int VEC>
-LaunchFn pick_t(int t, int w) {
+LaunchFn pick_t(int t, int w, int m) {
     switch (t) {
-        case 4: return pick_w<VEC, 4>(w);
-        case 8: return pick_w<VEC, 8>(w);
-        case 16:
-            if constexpr (VEC == 4) return nullptr;
-            else return pick_w<VEC, 16>(w);
+        case 4: return pick_w<VEC, 4>(w, m);
+        case 8: return pick_w<VEC, 8>(w, m);
+        case 16: return pick_w<VEC, 16>(w, m);
         default: return nullptr;
     }
 }
 
-LaunchFn pick_launch(const TileShape& s) { return s.vec == 4 ? pick_t<4>(s.t, s.w) : pick_t<1>(s.t, s.w); }
+LaunchFn pick_launch(const TileShape& s) {
+    return s.vec == 4 ? pick_t<4>(s.t, s.w, s.m) : pick_t<1>(s.t, s.w, s.m);
+}
 
 // ----------------------------------------------------------------------------- persistent grid
 
@@ -404,6 +442,7 @@ linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, l
     plan->chunks = p.tiles ? p.geom.nchunks : 0;
     plan->tiles = p.tiles;
     plan->workspace_bytes = p.workspace_bytes;
+    plan->mode = p.tile.m;
     return LINREC_OK;
 }
 
@@ -443,6 +482,15 @@ linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, i
 
     const LaunchFn fn = pick_launch(p.tile);
     if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
+    if (p.tile.m == 1) {
+        // one tile per workgroup; the hardware keeps as many resident as fit
+        (void)hipGetLastError();
+        fn->run(dim3(static_cast<uint32_t>(p.tiles)), dim3((p.tile.w + p.geom.carry_waves) * linrec::kWave), a, b, h,
+                p.geom, hdr, stat, hs);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
+        return LINREC_OK;
+    }
     const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
     int64_t resident = 0;
     if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;

@@ -49,17 +49,19 @@ constexpr int kLookbackWindow = 4;        // predecessors read per round trip
 constexpr uint32_t kKindAggregate = 1u;   // payload: one component of the tile pair
 constexpr uint32_t kKindInclusive = 2u;   // payload: state h at the tile's last step
 
-// Workspace: a header, kDoneSlots completion counters (one 128-byte line each),
-// then three status arrays (pair A, pair B, inclusive state) of nstatus words.
+// Workspace: a header, kDoneSlots slot lines (128 bytes each: word 0 counts
+// the workgroups of the current call that hold the epoch, word 1 is the epoch
+// of the current call), then three status arrays (pair A, pair B, inclusive
+// state) of nstatus words.
 constexpr int kLineWords = 32;    // uint32 words per 128-byte line
 constexpr int kDoneSlots = 256;
 
 struct WorkspaceHeader {
-    uint32_t epoch;                    // call counter used in status tags
+    uint32_t reserved;
     uint32_t pad0[kLineWords - 1];
     uint32_t timeouts;                 // waits resolved by recomputation (sticky)
     uint32_t pad1[kLineWords - 1];
-    uint32_t finished;                 // completion slots filled in the current call
+    uint32_t finished;                 // slot lines filled in the current call
     uint32_t pad2[kLineWords - 1];
     uint32_t pad3[kLineWords];
 };
@@ -317,13 +319,200 @@ __device__ inline float lookback_channel(const float* __restrict__ a, const floa
     return acc_b;
 }
 
-// LDS shared by the data waves and the carry wave of one workgroup.
+// ---------------------------------------------------------------------------
+// Call epochs.  Workgroup k of a call belongs to slot line k * kDoneSlots / grid
+// (contiguous ranges, so slots fill one after another during the call rather
+// than all at its end).  Each workgroup reads the epoch from its slot line and
+// then adds one to the line's count; the workgroup that fills a line adds one
+// to `finished`, and the one that fills that writes the next epoch into every
+// slot line.  By then every workgroup of the call holds its epoch, and the
+// next call on the stream cannot start before this one has ended, so the order
+// in which workgroups run does not matter.  Spreading reads and counts over
+// many lines keeps same-address traffic rare.
+
+__device__ __forceinline__ uint32_t* slot_line(WorkspaceHeader* hdr, int64_t slot) {
+    return reinterpret_cast<uint32_t*>(hdr + 1) + slot * kLineWords;
+}
+
+__device__ __forceinline__ int64_t slot_of(int64_t group, int64_t groups) { return group * kDoneSlots / groups; }
+
+// first workgroup of slot `slot` (ceil(slot * groups / kDoneSlots))
+__device__ __forceinline__ int64_t slot_begin(int64_t slot, int64_t groups) {
+    return (slot * groups + kDoneSlots - 1) / kDoneSlots;
+}
+
+__device__ __forceinline__ uint32_t call_epoch(WorkspaceHeader* hdr) {
+    return observe32(slot_line(hdr, slot_of(blockIdx.x, gridDim.x)) + 1);
+}
+
+// Lane 0 counts the workgroup in its slot line.  The addend is computed from
+// the epoch this workgroup read (epochs are below 2^30, so it is 1): the count
+// cannot be performed before that read has returned.  Returns the count
+// before the addition on lane 0, 0 elsewhere.
+__device__ __forceinline__ uint32_t count_in(WorkspaceHeader* hdr, uint32_t epoch, int lane) {
+    if (lane != 0) return 0u;
+    return __hip_atomic_fetch_add(slot_line(hdr, slot_of(blockIdx.x, gridDim.x)), 1u + (epoch >> 30),
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Whole wave: given count_in's result, rearm the slot line if this workgroup
+// filled it, and advance the epoch if it filled the last line.
+__device__ inline void count_done(WorkspaceHeader* hdr, uint32_t epoch, uint32_t before, int lane) {
+    const int64_t groups = gridDim.x;
+    const int64_t slot = slot_of(blockIdx.x, groups);
+    int last = 0;
+    if (lane == 0) {
+        const uint32_t expect = static_cast<uint32_t>(slot_begin(slot + 1, groups) - slot_begin(slot, groups));
+        if (before + 1 == expect) {
+            __hip_atomic_store(slot_line(hdr, slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t lines = static_cast<uint32_t>(groups < kDoneSlots ? groups : kDoneSlots);
+            const uint32_t f = __hip_atomic_fetch_add(&hdr->finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (f + 1 == lines) {
+                __hip_atomic_store(&hdr->finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = 1;
+            }
+        }
+    }
+    if (__shfl(last, 0) != 0) {
+        const uint32_t next = (epoch + 1u) & 0x3fffffffu;
+        for (int k = lane; k < kDoneSlots; k += kWave)
+            __hip_atomic_store(slot_line(hdr, k) + 1, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// LDS shared by the waves of one workgroup.
 template <int VEC, int W>
 struct TileShared {
     Vec<VEC> agg_a[W][kWave];   // pair of each data wave's steps, per lane channel group
     Vec<VEC> agg_b[W][kWave];
     float h_in[kWave * VEC];    // state entering the tile, per slab channel
 };
+
+// What a lane keeps of its tile between the scan in registers and the store.
+template <int VEC>
+struct LanePrefix {
+    Vec<VEC> ex_a, ex_b;   // pair of the steps before this lane's in its wave (group scan)
+};
+
+// Steps (2)-(4) up to the hand-over: per-lane composition, the group scan
+// along t inside the wave, and the wave's pair into LDS.  Inputs at t = 0 get
+// a = 0: the state before t = 0 is zero, so a_0 never contributes.
+template <int VEC, int T, int W>
+__device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, TileShared<VEC, W>& sh, const TileSpot& s,
+                                                          int lane, int wave, int quad, int grp, Vec<VEC> (&av)[T],
+                                                          const Vec<VEC> (&bv)[T]) {
+    if (s.t0 == 0) av[0] = splat<VEC>(0.0f);
+
+    // (2) per-lane sequential composition over the T steps
+    Vec<VEC> la = av[0], lb = bv[0];
+#pragma unroll
+    for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, av[j], bv[j]);
+
+    // (3) groups along t inside the wave: inclusive scan, then shift to exclusive
+    LanePrefix<VEC> pre;
+    pre.ex_a = splat<VEC>(1.0f);
+    pre.ex_b = splat<VEC>(0.0f);
+    Vec<VEC> wave_a = la, wave_b = lb;
+    if (g.groups > 1) {
+        Vec<VEC> in_a = la, in_b = lb;
+        for (int off = g.lanes_d; off < kWave; off <<= 1) {
+            const int src = (lane - off) & (kWave - 1);
+            const Vec<VEC> pa = lane_value<VEC>(in_a, src);
+            const Vec<VEC> pb = lane_value<VEC>(in_b, src);
+            if (lane >= off) after<VEC>(in_a, in_b, pa, pb);
+        }
+        const int prev = (lane - g.lanes_d) & (kWave - 1);
+        const Vec<VEC> pa = lane_value<VEC>(in_a, prev);
+        const Vec<VEC> pb = lane_value<VEC>(in_b, prev);
+        if (grp > 0) { pre.ex_a = pa; pre.ex_b = pb; }
+        const int last = (g.groups - 1) * g.lanes_d + quad;
+        wave_a = lane_value<VEC>(in_a, last);
+        wave_b = lane_value<VEC>(in_b, last);
+    }
+
+    // (4) the wave's pair into LDS
+    if (grp == 0) {
+        sh.agg_a[wave][quad] = wave_a;
+        sh.agg_b[wave][quad] = wave_b;
+    }
+    return pre;
+}
+
+// (4) after the hand-over barrier: the pair of the waves before this one.
+template <int VEC, int W>
+__device__ __forceinline__ void wave_prefix(TileShared<VEC, W>& sh, int wave, int quad, Vec<VEC>& pw_a, Vec<VEC>& pw_b) {
+    pw_a = splat<VEC>(1.0f);
+    pw_b = splat<VEC>(0.0f);
+    for (int v = 0; v < wave; ++v) then_apply<VEC>(pw_a, pw_b, sh.agg_a[v][quad], sh.agg_b[v][quad]);
+}
+
+// (6) once the state entering the tile is in LDS: the state entering this
+// lane's steps, then replay and store.  Stores past the end of the sequence
+// or of the channels are dropped.
+template <int VEC, int T, int W>
+__device__ __forceinline__ void replay_store(const TileShared<VEC, W>& sh, const TileSpot& s, int quad,
+                                             const LanePrefix<VEC>& pre, const Vec<VEC>& pw_a, const Vec<VEC>& pw_b,
+                                             const Vec<VEC> (&av)[T], const Vec<VEC> (&bv)[T]) {
+    Vec<VEC> hs;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+        hs.v[i] = sh.h_in[quad * VEC + i];
+        hs.v[i] = __builtin_fmaf(pw_a.v[i], hs.v[i], pw_b.v[i]);
+        hs.v[i] = __builtin_fmaf(pre.ex_a.v[i], hs.v[i], pre.ex_b.v[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(av[j].v[i], hs.v[i], bv[j].v[i]);
+        store_vec<VEC>(s.rh, s.off + j * s.step, hs);
+    }
+}
+
+// (5) for slab channel c of the tile (one per lane; the caller has passed the
+// hand-over barrier): fold the data waves' pairs into the tile pair, publish
+// it, look back for the state entering the tile, publish the state leaving
+// it, and put the entering state into LDS.
+template <int VEC, int W>
+__device__ __forceinline__ void carry_channel(const float* __restrict__ a, const float* __restrict__ b,
+                                              const Geometry& g, uint64_t* __restrict__ stat, TileShared<VEC, W>& sh,
+                                              int c, uint32_t epoch, bool& recomputed, int64_t tile) {
+    if (c >= g.slab_channels) return;
+    const int64_t chunk = tile / g.nseq;
+    const int64_t seq = tile - chunk * g.nseq;
+    const int64_t row = seq / g.nslab;
+    const int64_t slab = seq - row * g.nslab;
+    const int64_t d = slab * g.slab_channels + c;
+    float h_in = 0.0f;
+    if (g.nchunks > 1 && d < g.D) {
+        const bool has_successor = chunk + 1 < g.nchunks;
+        const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
+        const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
+        uint64_t* stat_a = stat;
+        uint64_t* stat_b = stat + g.nstatus;
+        uint64_t* stat_p = stat + 2 * g.nstatus;
+        const float* agg_a = &sh.agg_a[0][0].v[0];
+        const float* agg_b = &sh.agg_b[0][0].v[0];
+        float ta = agg_a[c], tb = agg_b[c];
+#pragma unroll
+        for (int v = 1; v < W; ++v) {
+            const float na = agg_a[v * kWave * VEC + c], nb = agg_b[v * kWave * VEC + c];
+            tb = __builtin_fmaf(na, tb, nb);
+            ta = na * ta;
+        }
+        // status entries are sequence-major: chunk j-1 of a sequence sits
+        // slab_channels entries before chunk j
+        const int64_t idx = (seq * g.nchunks + chunk) * g.slab_channels + c;
+        if (chunk > 0) {
+            if (has_successor) {
+                publish(stat_a + idx, tag_agg, ta);
+                publish(stat_b + idx, tag_agg, tb);
+            }
+            h_in = lookback_channel(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc, recomputed);
+        }
+        if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
+    }
+    sh.h_in[c] = h_in;
+}
 
 // Data wave, one tile of the persistent loop: start the loads of the
 // workgroup's next tile into (nav, nbv), scan the tile whose inputs are in
@@ -344,121 +533,26 @@ __device__ __forceinline__ void data_tile(const float* __restrict__ a, const flo
         if (next >= g.ntiles) ns.off = kOutOfRange;
         load_tile<VEC, T>(nav, nbv, ns);
     }
-
     const TileSpot s = locate(a, b, h, g, tile, wave, quad, grp, VEC, T);
-    // the state before t = 0 is zero, so a_0 never contributes: use 0 for it
-    if (s.t0 == 0) av[0] = splat<VEC>(0.0f);
-
-    // (2) per-lane sequential composition over the T steps
-    Vec<VEC> la = av[0], lb = bv[0];
-#pragma unroll
-    for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, av[j], bv[j]);
-
-    // (3) groups along t inside the wave: inclusive scan, then shift to exclusive
-    Vec<VEC> ex_a = splat<VEC>(1.0f), ex_b = splat<VEC>(0.0f);
-    Vec<VEC> wave_a = la, wave_b = lb;
-    if (g.groups > 1) {
-        Vec<VEC> in_a = la, in_b = lb;
-        for (int off = g.lanes_d; off < kWave; off <<= 1) {
-            const int src = (lane - off) & (kWave - 1);
-            const Vec<VEC> pa = lane_value<VEC>(in_a, src);
-            const Vec<VEC> pb = lane_value<VEC>(in_b, src);
-            if (lane >= off) after<VEC>(in_a, in_b, pa, pb);
-        }
-        const int prev = (lane - g.lanes_d) & (kWave - 1);
-        const Vec<VEC> pa = lane_value<VEC>(in_a, prev);
-        const Vec<VEC> pb = lane_value<VEC>(in_b, prev);
-        if (grp > 0) { ex_a = pa; ex_b = pb; }
-        const int last = (g.groups - 1) * g.lanes_d + quad;
-        wave_a = lane_value<VEC>(in_a, last);
-        wave_b = lane_value<VEC>(in_b, last);
-    }
-
-    // (4) wave pairs through LDS; per-wave exclusive prefix
-    if (grp == 0) {
-        sh.agg_a[wave][quad] = wave_a;
-        sh.agg_b[wave][quad] = wave_b;
-    }
+    const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
-    Vec<VEC> pw_a = splat<VEC>(1.0f), pw_b = splat<VEC>(0.0f);
-    for (int v = 0; v < wave; ++v) then_apply<VEC>(pw_a, pw_b, sh.agg_a[v][quad], sh.agg_b[v][quad]);
+    Vec<VEC> pw_a, pw_b;
+    wave_prefix<VEC, W>(sh, wave, quad, pw_a, pw_b);
     __syncthreads();   // the carry wave has written the state entering the tile
-
-    // (6) state entering this lane's steps, then replay and store
-    Vec<VEC> hs;
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-        hs.v[i] = sh.h_in[quad * VEC + i];
-        hs.v[i] = __builtin_fmaf(pw_a.v[i], hs.v[i], pw_b.v[i]);
-        hs.v[i] = __builtin_fmaf(ex_a.v[i], hs.v[i], ex_b.v[i]);
-    }
-    // stores past the end of the sequence or of the channels are dropped
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(av[j].v[i], hs.v[i], bv[j].v[i]);
-        store_vec<VEC>(s.rh, s.off + j * s.step, hs);
-    }
+    replay_store<VEC, T, W>(sh, s, quad, pre, pw_a, pw_b, av, bv);
 }
 
-// Carry wave, one tile: (5) for slab channel c (one per lane), fold the data
-// waves' pairs into the tile pair, publish it, look back for the state
-// entering the tile, publish the state leaving it, and hand the entering state
-// to the data waves.  Carry waves issue no data loads or stores, so their
-// status polls never queue behind the data traffic.
-template <int VEC, int W>
-__device__ __forceinline__ void carry_tile(const float* __restrict__ a, const float* __restrict__ b,
-                                           const Geometry& g, uint64_t* __restrict__ stat, TileShared<VEC, W>& sh,
-                                           int c, uint32_t epoch, bool& recomputed, int64_t tile) {
-    const int64_t chunk = tile / g.nseq;
-    const int64_t seq = tile - chunk * g.nseq;
-    const int64_t row = seq / g.nslab;
-    const int64_t slab = seq - row * g.nslab;
-    const bool chained = g.nchunks > 1;
-    const bool has_successor = chunk + 1 < g.nchunks;
-    const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
-    const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
-    uint64_t* stat_a = stat;
-    uint64_t* stat_b = stat + g.nstatus;
-    uint64_t* stat_p = stat + 2 * g.nstatus;
-    const float* agg_a = &sh.agg_a[0][0].v[0];
-    const float* agg_b = &sh.agg_b[0][0].v[0];
-
-    __syncthreads();   // wave pairs are in LDS
-    if (c < g.slab_channels) {
-        const int64_t d = slab * g.slab_channels + c;
-        float h_in = 0.0f;
-        if (chained && d < g.D) {
-            float ta = agg_a[c], tb = agg_b[c];
-#pragma unroll
-            for (int v = 1; v < W; ++v) {
-                const float na = agg_a[v * kWave * VEC + c], nb = agg_b[v * kWave * VEC + c];
-                tb = __builtin_fmaf(na, tb, nb);
-                ta = na * ta;
-            }
-            // status entries are sequence-major: chunk j-1 of a sequence sits
-            // slab_channels entries before chunk j
-            const int64_t idx = (seq * g.nchunks + chunk) * g.slab_channels + c;
-            if (chunk > 0) {
-                if (has_successor) {
-                    publish(stat_a + idx, tag_agg, ta);
-                    publish(stat_b + idx, tag_agg, tb);
-                }
-                h_in = lookback_channel(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc,
-                                        recomputed);
-            }
-            if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
-        }
-        sh.h_in[c] = h_in;
-    }
-    __syncthreads();   // the state entering the tile is in LDS
-}
+// Most threads a workgroup of W data waves and up to VEC carry waves may have
+// (the host never launches more than 1024).
+constexpr int group_limit(int w, int vec) { return (w + vec) * kWave < 1024 ? (w + vec) * kWave : 1024; }
 
 // Persistent workgroup of W data waves and carry_waves (<= VEC) carry waves.
 // Tiles blockIdx, blockIdx + grid, ... are taken in order; every wave runs the
-// same number of tiles and meets the same two barriers per tile.
+// same number of tiles and meets the same two barriers per tile.  Carry waves
+// issue no data loads or stores, so their status polls never queue behind the
+// data traffic (loads and stores retire in order per wave).
 template <int VEC, int T, int W>
-__global__ void __launch_bounds__((W + VEC) * kWave)
+__global__ void __launch_bounds__(group_limit(W, VEC))
 scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
            Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
     __shared__ TileShared<VEC, W> sh;
@@ -470,37 +564,19 @@ scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __re
 
     if (wave >= W) {
         const int carry = wave - W;
-        const uint32_t epoch = chained ? observe32(&hdr->epoch) : 0u;
-        bool recomputed = false;
-        for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride)
-            carry_tile<VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
-        if (!chained) return;
-        if (__ballot(recomputed) != 0 && lane == 0)
-            __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (carry != 0) return;
-        // Completion count: workgroup k reports to slot k % kDoneSlots; the one
-        // that fills a slot reports to `finished`, and the one that fills that
-        // rearms the header (next epoch) for the following call.  Spreading the
-        // count over many lines keeps same-address atomics rare.
-        if (lane == 0) {
-            uint32_t* done = reinterpret_cast<uint32_t*>(hdr + 1);
-            const int64_t groups = gridDim.x;
-            const int64_t slot = blockIdx.x % kDoneSlots;
-            const uint32_t expect = static_cast<uint32_t>(groups / kDoneSlots + (slot < groups % kDoneSlots ? 1 : 0));
-            uint32_t* ctr = done + slot * kLineWords;
-            const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (prev + 1 == expect) {
-                __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const uint32_t slots = static_cast<uint32_t>(groups < kDoneSlots ? groups : kDoneSlots);
-                const uint32_t f =
-                    __hip_atomic_fetch_add(&hdr->finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (f + 1 == slots) {
-                    __hip_atomic_store(&hdr->finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&hdr->epoch, (epoch + 1u) & 0x3fffffffu, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-            }
+        uint32_t epoch = 0;
+        if (chained) {
+            epoch = call_epoch(hdr);
+            if (carry == 0) count_done(hdr, epoch, count_in(hdr, epoch, lane), lane);
         }
+        bool recomputed = false;
+        for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride) {
+            __syncthreads();   // wave pairs are in LDS
+            carry_channel<VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+            __syncthreads();   // the state entering the tile is in LDS
+        }
+        if (chained && __ballot(recomputed) != 0 && lane == 0)
+            __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -522,6 +598,55 @@ scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __re
         data_tile<VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
         tile += stride;
     }
+}
+
+// One tile per workgroup (grid = number of tiles) of W data waves and
+// carry_waves carry waves: the data waves load, scan in registers and hand
+// over through LDS; the carry waves look back for the tile's channels, one
+// per lane; the data waves replay and store.  Keeping the lookback out of the
+// data waves keeps their register count, and so the number of workgroups
+// resident per CU, down; with many resident, the loads of some overlap the
+// lookback of others.
+template <int VEC, int T, int W>
+__global__ void __launch_bounds__(group_limit(W, VEC))
+scan_one(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
+         Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
+    __shared__ TileShared<VEC, W> sh;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int64_t tile = blockIdx.x;
+    const bool chained = g.nchunks > 1;
+
+    if (wave >= W) {
+        const int carry = wave - W;
+        uint32_t epoch = 0, before = 0;
+        if (chained) {
+            epoch = call_epoch(hdr);
+            if (carry == 0) before = count_in(hdr, epoch, lane);
+        }
+        bool recomputed = false;
+        __syncthreads();   // wave pairs are in LDS
+        carry_channel<VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+        __syncthreads();   // the state entering the tile is in LDS
+        if (!chained) return;
+        if (__ballot(recomputed) != 0 && lane == 0)
+            __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (carry == 0) count_done(hdr, epoch, before, lane);
+        return;
+    }
+
+    const int quad = lane & (g.lanes_d - 1);
+    const int grp = lane >> g.log2_lanes_d;
+    const TileSpot s = locate(a, b, h, g, tile, wave, quad, grp, VEC, T);
+    Vec<VEC> av[T], bv[T];
+    load_tile<VEC, T>(av, bv, s);
+    const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
+    __syncthreads();   // wave pairs are in LDS
+    __syncthreads();   // the state entering the tile is in LDS
+    Vec<VEC> pw_a, pw_b;
+    wave_prefix<VEC, W>(sh, wave, quad, pw_a, pw_b);
+    replay_store<VEC, T, W>(sh, s, quad, pre, pw_a, pw_b, av, bv);
 }
 
 // Zero-fill used to (re)initialise a workspace; a kernel rather than a memset

@@ -46,6 +46,7 @@ class linrec_plan(ctypes.Structure):
         ("chunks", ctypes.c_int64),
         ("tiles", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
+        ("mode", ctypes.c_int32),
     ]
 
 

@@ -109,7 +109,15 @@ def test_tile_override(tile_env):
     os.environ["LINREC_TILE"] = "p=8,t=8,w=4,q=2"
     p = binding.linrec_scan_plan(32, 4096, 256)
     assert p["lanes_per_row"] == 8 and p["steps_per_tile"] == 8 * 4 * (64 // 8)
-    for bad in ("t=5", "w=3", "w=16", "vec=2", "t=16", "x=1", "t", "t=abc", "p=3", "p=128", "p=0",
+    os.environ["LINREC_TILE"] = "m=1,vec=4,t=16,w=2"
+    p = binding.linrec_scan_plan(32, 4096, 256)
+    assert (p["mode"], p["steps_per_lane"], p["waves"]) == (1, 16, 2)
+    os.environ["LINREC_TILE"] = "w=15,p=32"        # 15 data waves + 2 carry waves > 1024 threads
+    with pytest.raises(binding.LinrecError):
+        binding.linrec_scan_plan(32, 4096, 256)
+    os.environ["LINREC_TILE"] = "w=15,p=16"
+    assert binding.linrec_scan_plan(32, 4096, 256)["waves"] == 15
+    for bad in ("t=5", "w=3", "w=16", "w=5", "vec=2", "t=16", "m=2", "w=14,t=8", "m=-1", "m=0,vec=4,t=16", "x=1", "t", "t=abc", "p=3", "p=128", "p=0",
                 "q=-1", "q=65", "d=1"):
         os.environ["LINREC_TILE"] = bad
         with pytest.raises(binding.LinrecError) as err:

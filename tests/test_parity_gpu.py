@@ -99,13 +99,17 @@ def test_length_one_is_exact(lr):
 
 
 def supported_tiles():
+    """(vec, t, w, m) of every kernel instantiation; m = 0 persistent, m = 1 one tile per workgroup."""
     out = []
-    for vec in (1, 4):
-        for t in (4, 8, 16):
-            for w in (1, 2, 4, 8):
-                if vec == 4 and t == 16:
-                    continue
-                out.append((vec, t, w))
+    for m in (0, 1):
+        for vec in (1, 4):
+            for t in (4, 8, 16):
+                for w in (1, 2, 4, 6, 7, 8, 14, 15):
+                    if m == 0 and vec == 4 and t == 16:
+                        continue
+                    if w >= 14 and vec * t > 16:
+                        continue
+                    out.append((vec, t, w, m))
     return out
 
 
@@ -119,27 +123,44 @@ def tile_env():
         os.environ["LINREC_TILE"] = old
 
 
-@pytest.mark.parametrize("p", [1, 2, 4, 8, 16, 32])
-def test_lanes_per_row(lr, p, tile_env):
+@pytest.mark.parametrize("m", [0, 1])
+@pytest.mark.parametrize("p", [1, 2, 4, 8, 16, 32, 64])
+def test_lanes_per_row(lr, p, m, tile_env):
     """Narrower channel slabs (fewer lanes per row, more rows per wave instruction)."""
-    os.environ["LINREC_TILE"] = f"p={p}"
+    os.environ["LINREC_TILE"] = f"p={p},m={m},w=8"
     for shape in ((3, 2999, 136), (2, 1501, 256), (1, 777, 24)):
         a, b = li.make_inputs(*shape, seed=shape[1] + p, a_lo=0.5, a_hi=1.0)
         plan = lr.linrec_scan_plan(*shape)
-        assert plan["lanes_per_row"] <= p
-        check_case(lr, a, b, f"p={p} {shape} chunks={plan['chunks']}")
+        assert plan["lanes_per_row"] <= p and plan["mode"] == m
+        check_case(lr, a, b, f"p={p} m={m} {shape} chunks={plan['chunks']}")
 
 
-@pytest.mark.parametrize("tile", supported_tiles(), ids=lambda t: f"vec{t[0]}_t{t[1]}_w{t[2]}")
+@pytest.mark.parametrize("tile", supported_tiles(), ids=lambda t: f"vec{t[0]}_t{t[1]}_w{t[2]}_m{t[3]}")
 def test_every_tile_shape(lr, tile, tile_env):
     """Each kernel instantiation on ragged shapes that span many tiles along L."""
-    vec, t, w = tile
-    os.environ["LINREC_TILE"] = f"vec={vec},t={t},w={w}"
+    vec, t, w, m = tile
+    p = ",p=16" if w == 15 and vec == 4 else ""
+    os.environ["LINREC_TILE"] = f"vec={vec},t={t},w={w},m={m}{p}"
     for shape in ((3, 2999, 136), (2, 3001, 24), (1, 1500, 1 if vec == 1 else 4)):
         a, b = li.make_inputs(*shape, seed=shape[1] + vec + t + w, a_lo=0.5, a_hi=1.0)
         plan = lr.linrec_scan_plan(*shape)
-        assert (plan["vec"], plan["steps_per_lane"], plan["waves"]) == (vec, t, w)
+        assert (plan["vec"], plan["steps_per_lane"], plan["waves"], plan["mode"]) == (vec, t, w, m)
         check_case(lr, a, b, f"tile {tile} {shape} chunks={plan['chunks']}")
+
+
+def test_modes_and_grids_alternate_on_one_workspace(lr, tile_env):
+    """Consecutive calls with different kernels and grid sizes share the device workspace; each
+    call's status words must carry a fresh epoch (a stale word accepted as current would show up
+    as a wrong carry)."""
+    cases = [("m=0", (4, 3000, 256)), ("m=1", (4, 3000, 256)), ("m=1,t=8,w=2", (2, 9000, 64)),
+             ("m=0,w=2", (2, 9000, 64)), ("m=1", (4, 3000, 256)), ("m=0", (1, 70000, 8)),
+             ("m=1,p=64,w=8", (3, 5000, 256)), ("m=0", (4, 3000, 256))]
+    for k, (spec, shape) in enumerate(cases):
+        os.environ["LINREC_TILE"] = spec
+        a, b = li.make_inputs(*shape, seed=500 + k, a_lo=0.9, a_hi=1.0)
+        plan = lr.linrec_scan_plan(*shape)
+        assert plan["chunks"] > 1
+        check_case(lr, a, b, f"call {k} {spec} {shape} tiles={plan['tiles']}")
 
 
 def test_misaligned_buffers_take_the_scalar_form(lr):
@@ -227,10 +248,12 @@ def spin_env():
         os.environ["LINREC_SPIN_LIMIT"] = old
 
 
-def test_spin_limit_zero_recomputes_and_stays_exact(lr, spin_env):
+@pytest.mark.parametrize("m", [0, 1])
+def test_spin_limit_zero_recomputes_and_stays_exact(lr, spin_env, tile_env, m):
     """With the wait for a predecessor forced to zero polls, every tile that finds its predecessor's
     status not yet published recomputes that predecessor's pair from a and b.  The output must not
     change beyond the bar, and every kernel exits normally."""
+    os.environ["LINREC_TILE"] = f"m={m}"
     for shape, lo in (((2, 8192, 64), 0.9), ((4, 2048, 256), 0.0)):
         a_np, b_np = li.make_inputs(*shape, seed=9, a_lo=lo, a_hi=1.0)
         ref = oracle.linrec_oracle_f64(a_np, b_np)
@@ -240,7 +263,7 @@ def test_spin_limit_zero_recomputes_and_stays_exact(lr, spin_env):
         os.environ.pop("LINREC_SPIN_LIMIT")
         recomputed = lr.linrec_device_timeouts() - before
         worst, where = error_ratio(h, ref)
-        say(f"[recompute] {shape}: {recomputed} tiles recomputed a predecessor; max ratio {worst:.3e}")
+        say(f"[recompute] m={m} {shape}: {recomputed} tiles recomputed a predecessor; max ratio {worst:.3e}")
         assert worst <= TOL, (worst, where)
         # the normal path afterwards
         h = run_gpu(lr, a_np, b_np)
