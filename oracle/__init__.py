@@ -39,12 +39,12 @@ def build(source: Path = SOURCE, output: Path = LIBRARY, extra_flags=()) -> Path
 
 
 def load_library(path: Path | str) -> ctypes.CDLL:
-    """Load an oracle shared library and declare its one entry point."""
+    """Load an oracle shared library and declare its entry points."""
     lib = ctypes.CDLL(str(path))
-    fn = lib.linrec_oracle_f64
-    fn.restype = ctypes.c_int
-    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    for fn in (lib.linrec_oracle_f64, lib.linrec_oracle_rev_f64):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
     return lib
 
 
@@ -66,8 +66,10 @@ def default_threads() -> int:
     return max(1, min(16, n))
 
 
-def call_library(lib: ctypes.CDLL, a: np.ndarray, b: np.ndarray, h_init=None, threads=None) -> np.ndarray:
-    """Run ``lib``'s oracle on fp32 (B, L, D) arrays; returns float64 (B, L, D)."""
+def call_library(lib: ctypes.CDLL, a: np.ndarray, b: np.ndarray, h_init=None, threads=None,
+                 reverse: bool = False) -> np.ndarray:
+    """Run ``lib``'s oracle (the reverse-time form if ``reverse``) on fp32 (B, L, D) arrays;
+    returns float64 (B, L, D)."""
     a = np.ascontiguousarray(a, dtype=np.float32)
     b = np.ascontiguousarray(b, dtype=np.float32)
     if a.ndim != 3 or a.shape != b.shape:
@@ -79,7 +81,8 @@ def call_library(lib: ctypes.CDLL, a: np.ndarray, b: np.ndarray, h_init=None, th
         if hi.shape != (B, D):
             raise ValueError(f"h_init must be (B, D) = {(B, D)}, got {hi.shape}")
     h = np.empty((B, L, D), dtype=np.float64)
-    rc = lib.linrec_oracle_f64(a.ctypes.data, b.ctypes.data,
+    fn = lib.linrec_oracle_rev_f64 if reverse else lib.linrec_oracle_f64
+    rc = fn(a.ctypes.data, b.ctypes.data,
                                None if hi is None else hi.ctypes.data,
                                h.ctypes.data, B, L, D,
                                default_threads() if threads is None else int(threads))
@@ -95,3 +98,13 @@ def linrec_oracle_f64(a: np.ndarray, b: np.ndarray, h_init=None, threads=None) -
     h_0 = a_0 * h_init + b_0; without it the state is zero and h_0 = b_0.
     """
     return call_library(_library(), a, b, h_init=h_init, threads=threads)
+
+
+def linrec_oracle_rev_f64(a: np.ndarray, b: np.ndarray, h_init=None, threads=None) -> np.ndarray:
+    """float64 reference of the reverse-time recurrence h_t = a_t * h_{t+1} + b_t for fp32 inputs
+    of shape (B, L, D), run from t = L-1 down to 0.
+
+    ``h_init`` (B, D), when given, is the state after the last step, so that
+    h_{L-1} = a_{L-1} * h_init + b_{L-1}; without it the state is zero and h_{L-1} = b_{L-1}.
+    """
+    return call_library(_library(), a, b, h_init=h_init, threads=threads, reverse=True)

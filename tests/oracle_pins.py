@@ -337,6 +337,137 @@ def pin_equivariance(f):
     _bitwise(f(ap, bp), h[pb][:, :, pd], "permutation equivariance")
 
 
+# --------------------------------------------------------------------------- reverse-time form
+#
+# The reverse-time recurrence h_t = a_t * h_{t+1} + b_t (t = L-1 .. 0, zero state after the last
+# step) is not on the pages; it is the time reversal of their definition and the recurrence of the
+# scan's gradient.  Each ``pin_rev_*`` takes the reverse oracle ``f_rev(a, b, h_init=None)`` and the
+# forward oracle ``f_fwd`` (already pinned above) and checks f_rev against mathematics that does not
+# go through its own loop.
+
+
+def exact_reverse_closed_form(a_col, b_col):
+    """Exact rational h for one channel: h_t = sum_{s>=t} b_s * prod_{r=t..s-1} a_r."""
+    af = [Fraction(float(x)) for x in a_col]
+    bf = [Fraction(float(x)) for x in b_col]
+    L = len(bf)
+    out = []
+    for t in range(L):
+        total, prod = Fraction(0), Fraction(1)
+        for s in range(t, L):
+            total += bf[s] * prod
+            prod *= af[s]
+        out.append(total)
+    return out
+
+
+def pin_rev_closed_form(f_rev, f_fwd):
+    """Time-varying a, evaluated exactly in rationals; a_{L-1} multiplies the zero state only."""
+    rng = _rng(201)
+    B, L, D = 2, 20, 3
+    a = (rng.random((B, L, D), dtype=np.float32) * np.float32(3.0) - np.float32(1.5)).astype(np.float32)
+    b = _normal(rng, (B, L, D))
+    ref = np.empty((B, L, D))
+    for bi in range(B):
+        for d in range(D):
+            ref[bi, :, d] = [float(x) for x in exact_reverse_closed_form(a[bi, :, d], b[bi, :, d])]
+    _close(f_rev(a, b), ref, 1e-12, "reverse closed form")
+    a[:, -1, :] = np.float32(np.inf)
+    _close(f_rev(a, b), ref, 1e-12, "reverse: a_{L-1} never used from a zero state")
+
+
+def pin_rev_adjoint(f_rev, f_fwd):
+    """The reverse recurrence over g with a shifted one step is the adjoint of the forward scan in b:
+    per channel, sum_t g_t * fwd(a, b)_t == sum_t rev(a', g)_t * b_t with a'_t = a_{t+1}.  This is
+    what makes it the gradient dLoss/db for g = dLoss/dh."""
+    rng = _rng(202)
+    B, L, D = 3, 300, 5
+    a = (rng.random((B, L, D), dtype=np.float32) * np.float32(2.2) - np.float32(1.1)).astype(np.float32)
+    b = _normal(rng, (B, L, D))
+    g = _normal(rng, (B, L, D))
+    a_next = np.zeros_like(a)
+    a_next[:, :-1, :] = a[:, 1:, :]
+    h = f_fwd(a, b)
+    y = f_rev(a_next, g)
+    lhs = np.sum(g.astype(np.float64) * h, axis=1)
+    rhs = np.sum(y * b.astype(np.float64), axis=1)
+    scale = np.sum(np.abs(g.astype(np.float64) * h), axis=1) + np.sum(np.abs(y * b.astype(np.float64)), axis=1)
+    rel = np.abs(lhs - rhs) / scale
+    assert float(rel.max()) <= 1e-12, f"adjoint identity: {float(rel.max()):.3e}"
+
+
+def pin_rev_zero_a(f_rev, f_fwd):
+    rng = _rng(203)
+    b = _normal(rng, (3, 29, 4))
+    _bitwise(f_rev(np.zeros_like(b), b), b, "reverse a=0 -> h=b")
+
+
+def pin_rev_unit_a_suffix_sum(f_rev, f_fwd):
+    """a == 1: h_t is the suffix sum of b from t on, compared with math.fsum."""
+    rng = _rng(204)
+    B, L, D = 2, 250, 3
+    b = _normal(rng, (B, L, D))
+    ref = np.empty((B, L, D))
+    for bi in range(B):
+        for d in range(D):
+            col = b[bi, :, d].astype(np.float64).tolist()
+            for t in range(L):
+                ref[bi, t, d] = math.fsum(col[t:])
+    _close(f_rev(np.ones_like(b), b), ref, 1e-12, "reverse a=1 -> suffix sum")
+
+
+def pin_rev_split_carry(f_rev, f_fwd):
+    """Scanning [0, k) backward from the state h_k reproduces the head of the full reverse scan
+    exactly; a given final state enters as h_{L-1} = a_{L-1} * h_init + b_{L-1}."""
+    rng = _rng(205)
+    B, L, D = 2, 60, 5
+    a = (rng.random((B, L, D), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)).astype(np.float32)
+    b = _normal(rng, (B, L, D))
+    h = f_rev(a, b)
+    for k in (1, 23, 59):
+        head = f_rev(np.ascontiguousarray(a[:, :k]), np.ascontiguousarray(b[:, :k]), h_init=h[:, k])
+        _bitwise(head, h[:, :k], f"reverse split at {k}")
+    hi = _normal(rng, (B, D)).astype(np.float64)
+    last = f_rev(a, b, h_init=hi)[:, -1, :]
+    ref = np.array([[float(Fraction(float(a[i, -1, d])) * Fraction(float(hi[i, d])) + Fraction(float(b[i, -1, d])))
+                     for d in range(D)] for i in range(B)])
+    _close(last, ref, 1e-15, "reverse: last step from a given state")
+
+
+def pin_rev_anticausal(f_rev, f_fwd):
+    """Changing inputs before t0 leaves h from t0 on bitwise unchanged."""
+    rng = _rng(206)
+    B, L, D = 2, 50, 3
+    a = rng.random((B, L, D), dtype=np.float32)
+    b = _normal(rng, (B, L, D))
+    h = f_rev(a, b)
+    t0 = 19
+    a2, b2 = a.copy(), b.copy()
+    a2[:, :t0] = rng.random((B, t0, D), dtype=np.float32) * np.float32(3.0)
+    b2[:, :t0] = _normal(rng, (B, t0, D))
+    _bitwise(f_rev(a2, b2)[:, t0:], h[:, t0:], "anti-causality")
+
+
+def pin_rev_length_one_and_empty(f_rev, f_fwd):
+    rng = _rng(207)
+    b = _normal(rng, (3, 1, 4))
+    _bitwise(f_rev(np.full_like(b, np.float32(np.inf)), b), b, "reverse L=1 -> h=b")
+    for shape in ((0, 5, 3), (2, 0, 3), (2, 5, 0)):
+        z = np.zeros(shape, np.float32)
+        assert f_rev(z, z.copy()).shape == shape
+
+
+REV_PINS = [
+    pin_rev_closed_form,
+    pin_rev_adjoint,
+    pin_rev_zero_a,
+    pin_rev_unit_a_suffix_sum,
+    pin_rev_split_carry,
+    pin_rev_anticausal,
+    pin_rev_length_one_and_empty,
+]
+
+
 ALL_PINS = [
     pin_zero_a,
     pin_unit_a_prefix_sum,

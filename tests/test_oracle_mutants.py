@@ -35,10 +35,38 @@ C_MUTANTS = {
 }
 
 
+REV_RECURRENCE = "rht[d] = (double)rat[d] * hnext[d] + (double)rbt[d];"
+
+# mistakes in the reverse-time loop; caught by the reverse pins
+REV_MUTANTS = {
+    "rev_dropped_b_term": (REV_RECURRENCE, "rht[d] = (double)rat[d] * hnext[d];"),
+    "rev_a_b_transposed": (REV_RECURRENCE, "rht[d] = (double)rbt[d] * hnext[d] + (double)rat[d];"),
+    "rev_a_index_shift": ("const float *rat = rab + t * D;", "const float *rat = rab + (t + 1) * D;"),
+    "rev_stale_state_two_ahead": ("const double *hnext = rhb + (t + 1) * D;",
+                                  "const double *hnext = rhb + (t + 2 < L ? t + 2 : t + 1) * D;"),
+    "rev_final_state_uses_a": ("rhb[last + d] = (double)rbb[last + d];",
+                               "rhb[last + d] = (double)rab[last + d] + (double)rbb[last + d];"),
+    "rev_carry_skips_a": ("rhb[last + d] = (double)rab[last + d] * h_init[bi * D + d] + (double)rbb[last + d];",
+                          "rhb[last + d] = h_init[bi * D + d] + (double)rbb[last + d];"),
+    "rev_wrong_batch_stride": ("const float *rbb = b_in + bi * L * D;", "const float *rbb = b_in + bi * D;"),
+    "rev_fp32_accumulation": (REV_RECURRENCE,
+                              "rht[d] = (double)(float)((float)rat[d] * (float)hnext[d] + (float)rbt[d]);"),
+}
+
+
 def _first_failing_pin(fn):
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(fn)
+        except AssertionError:
+            return pin.__name__
+    return None
+
+
+def _first_failing_rev_pin(f_rev, f_fwd):
+    for pin in oracle_pins.REV_PINS:
+        try:
+            pin(f_rev, f_fwd)
         except AssertionError:
             return pin.__name__
     return None
@@ -54,6 +82,19 @@ def test_c_mutant_is_caught(name, tmp_path):
     lib = oracle.load_library(oracle.build(mutant_c, tmp_path / f"lib{name}.so"))
     caught = _first_failing_pin(partial(oracle.call_library, lib))
     assert caught is not None, f"mutant {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(REV_MUTANTS))
+def test_reverse_c_mutant_is_caught(name, tmp_path):
+    old, new = REV_MUTANTS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation target not found exactly once: {old!r}"
+    mutant_c = tmp_path / f"{name}.c"
+    mutant_c.write_text(src.replace(old, new))
+    lib = oracle.load_library(oracle.build(mutant_c, tmp_path / f"lib{name}.so"))
+    f_rev = partial(oracle.call_library, lib, reverse=True)
+    caught = _first_failing_rev_pin(f_rev, oracle.linrec_oracle_f64)
+    assert caught is not None, f"mutant {name} passed every reverse pin"
 
 
 def _reversed_combine_oracle(a, b, h_init=None):
@@ -85,3 +126,4 @@ def test_unmodified_copy_passes(tmp_path):
     c.write_text(oracle.SOURCE.read_text())
     lib = oracle.load_library(oracle.build(c, tmp_path / "libcopy.so"))
     assert _first_failing_pin(partial(oracle.call_library, lib)) is None
+    assert _first_failing_rev_pin(partial(oracle.call_library, lib, reverse=True), oracle.linrec_oracle_f64) is None
