@@ -17,6 +17,8 @@
  * The result is any valid bracketing of that scan in fp32 with fused
  * multiply-add, so it is not bitwise unique; it matches a float64 sequential
  * evaluation within 1e-4 * (1 + |h|) per element on the tested workloads.
+ * linrec_scan_ex adds strided operands, bf16/fp16 storage, an initial and a
+ * final state, and the reverse-time form.
  *
  * All entry points are host functions; apart from linrec_device_timeouts and
  * linrec_release, none of them synchronises the device.
@@ -36,7 +38,7 @@ typedef enum linrec_status {
     LINREC_OK = 0,                  /* done, or enqueued on the stream                        */
     LINREC_ERR_INVALID_ARGUMENT = 1,/* negative size, size overflow, null or non-device buffer,
                                        buffer too small for B*L*D floats, or device mismatch   */
-    LINREC_ERR_OVERLAP = 2,         /* h overlaps a or b                                      */
+    LINREC_ERR_OVERLAP = 2,         /* an output buffer overlaps another buffer               */
     LINREC_ERR_HIP = 3,             /* a HIP runtime call or the kernel launch failed         */
     LINREC_ERR_OUT_OF_MEMORY = 4    /* the internal workspace could not be allocated          */
 } linrec_status;
@@ -62,8 +64,9 @@ typedef enum linrec_status {
  * grows when a larger shape needs more, and frees in linrec_release().  Calls
  * on one device share it, so calls that may overlap in time on one device
  * must be ordered on one stream; calls on different streams of one device
- * race.  Any alignment works: 16-byte aligned buffers with D % 4 == 0 use
- * 128-bit accesses, anything else the 32-bit form of the same kernel.
+ * race.  Buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
+ * aligned buffers with D % 4 == 0 use 128-bit accesses, anything else the
+ * 32-bit form of the same kernel.
  *
  * Errors: returns a status and never aborts; the message for the calling
  * thread's last failure is linrec_last_error_message().  LINREC_OK means the
@@ -108,6 +111,83 @@ typedef struct linrec_plan {
  * overflowing sizes, an unsupported LINREC_TILE or a null plan.
  */
 linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan *plan);
+
+/* Storage type of a, b and h in linrec_scan_ex (arithmetic is always fp32). */
+typedef enum linrec_dtype {
+    LINREC_F32 = 0,   /* IEEE binary32                                                  */
+    LINREC_BF16 = 1,  /* bfloat16: widened exactly on load, rounded to nearest even on store */
+    LINREC_F16 = 2    /* IEEE binary16: same; values beyond its range become infinite    */
+} linrec_dtype;
+
+/* One (B, L, D) operand: element (i, t, d) at ptr[i*stride_b + t*stride_l + d],
+ * strides in elements of the operand's storage type, each >= 0 (0 repeats a
+ * row: e.g. one decay a shared by every batch row). */
+typedef struct linrec_operand {
+    const void *ptr;
+    int64_t stride_b;
+    int64_t stride_l;
+} linrec_operand;
+
+/*
+ * linrec_scan_desc -- a generalised linrec_scan.
+ *
+ *   B, L, D   sizes, each >= 0.
+ *   dtype     linrec_dtype of a, b and h.
+ *   reverse   0: the recurrence runs forward in t, as in linrec_scan.
+ *             1: it runs backward: h[i,L-1,d] = b[i,L-1,d] and
+ *                h[i,t,d] = a[i,t,d] * h[i,t+1,d] + b[i,t,d] for t = L-2 .. 0
+ *                (the time reversal of the recurrence; over an incoming
+ *                gradient g with a shifted one step, a'[t] = a[t+1], it gives
+ *                dLoss/db of a forward scan).  Not on the pages that define
+ *                the forward recurrence.
+ *   a, b, h   operands; h.ptr is written (cast away its const).  h's rows
+ *             (i, t) must not overlap one another, and h must not overlap a
+ *             or b (a and b may overlap each other).
+ *   h_init    NULL, or a (B, D) row-major fp32 device buffer: the state before
+ *             the first step of the scan order, so that the first step is
+ *             h = a * h_init + b instead of h = b (forward: t = 0; reverse:
+ *             t = L-1).  This generalises the running carry between chunks
+ *             of the pages' kernels (the running-carry passage of the first
+ *             reasoning block of the Kimi-K2.6 l1_p9 transcript) to a carry
+ *             between calls.
+ *   h_final   NULL, or a (B, D) row-major fp32 device buffer that receives
+ *             the state after the last step (forward: h[:, L-1, :]; reverse:
+ *             h[:, 0, :]) before rounding to dtype; with L == 0 it receives
+ *             h_init (or zeros).  Scanning a long sequence in pieces, each
+ *             piece's h_final passed as the next one's h_init, gives the same
+ *             result as one call within rounding.  Must not overlap any other
+ *             buffer; h_init must not overlap h.
+ *
+ * 128-bit (fp32) or 64-bit (16-bit) accesses are used when D % 4 == 0, every
+ * stride is a multiple of 4 and a, b, h are aligned to 4 elements; anything
+ * else takes the one-channel-per-lane form of the same kernels.
+ */
+typedef struct linrec_scan_desc {
+    int64_t B, L, D;
+    int32_t dtype;
+    int32_t reverse;
+    linrec_operand a, b, h;
+    const float *h_init;
+    float *h_final;
+} linrec_scan_desc;
+
+/*
+ * linrec_scan_ex -- the scan described by *desc, enqueued on `stream`.
+ * Ownership, workspace, errors and environment as for linrec_scan; every
+ * buffer is checked to lie inside one device allocation of the current
+ * device that holds the elements the strides reach.  Returns
+ * LINREC_ERR_INVALID_ARGUMENT for a null desc, bad sizes, strides or dtype,
+ * rows of h that overlap one another, a, b or h not aligned to its element
+ * size, h_init or h_final not aligned to 4 bytes, a tile of an operand that
+ * would span 1 GiB or more (huge time strides), or bad buffers;
+ * LINREC_ERR_OVERLAP when a written buffer overlaps another one.
+ */
+linrec_status linrec_scan_ex(const linrec_scan_desc *desc, void *stream);
+
+/* linrec_scan_ex_plan -- fills *plan for linrec_scan_ex(desc) (pure host
+ * arithmetic on the sizes, strides, dtype and pointer alignment; no HIP call,
+ * buffers are not checked). */
+linrec_status linrec_scan_ex_plan(const linrec_scan_desc *desc, linrec_plan *plan);
 
 /* Static English text for a status code; "unknown status" for other values. */
 const char *linrec_status_string(int status);

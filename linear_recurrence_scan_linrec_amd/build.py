@@ -1,8 +1,9 @@
 """Build the gfx950 shared library ``liblinrec.so`` in-tree with hipcc.
 
-``python -m linear_recurrence_scan_linrec_amd.build`` compiles
-``csrc/linrec.hip`` (kernels and the C ABI of ``include/linrec.h``) into
-``linear_recurrence_scan_linrec_amd/lib/liblinrec.so``.
+``python -m linear_recurrence_scan_linrec_amd.build`` compiles the host side of
+the C ABI of ``include/linrec.h`` (``csrc/linrec.hip``) and the kernel instances
+for each storage type (``csrc/kernels_{f32,bf16,f16}.hip``) in parallel, then
+links them into ``linear_recurrence_scan_linrec_amd/lib/liblinrec.so``.
 """
 from __future__ import annotations
 
@@ -10,13 +11,16 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PACKAGE = Path(__file__).resolve().parent
 ROOT = PACKAGE.parent
 INCLUDE = ROOT / "include"
-SOURCES = [PACKAGE / "csrc" / "linrec.hip"]
-DEPENDS = SOURCES + [PACKAGE / "csrc" / "scan_kernel.hpp", INCLUDE / "linrec.h"]
+CSRC = PACKAGE / "csrc"
+SOURCES = [CSRC / "linrec.hip", CSRC / "kernels_f32.hip", CSRC / "kernels_bf16.hip", CSRC / "kernels_f16.hip"]
+DEPENDS = SOURCES + [CSRC / "scan_kernel.hpp", CSRC / "launch.hpp", CSRC / "instances.hpp", INCLUDE / "linrec.h"]
 LIBRARY = PACKAGE / "lib" / "liblinrec.so"
 ARCH = "gfx950"
 
@@ -25,7 +29,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # keep hipcc from forming packed-fp32 instructions (the host pass warns about
     # the unknown feature; that is expected)
@@ -40,17 +43,29 @@ def hipcc() -> str:
     return found
 
 
-def build(output: Path = LIBRARY, extra_flags=(), verbose: bool = False) -> Path:
-    """Compile the library; always recompiles."""
-    output.parent.mkdir(parents=True, exist_ok=True)
-    tmp = output.with_suffix(".so.tmp")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", *map(str, SOURCES), "-o", str(tmp)]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout + proc.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}")
+        raise RuntimeError(f"hipcc failed with exit code {proc.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build(output: Path = LIBRARY, extra_flags=(), verbose: bool = False) -> Path:
+    """Compile the library; always recompiles."""
+    output.parent.mkdir(parents=True, exist_ok=True)
+    tmp = output.with_suffix(".so.tmp")
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="linrec_build_") as work:
+        objects = [Path(work) / (src.stem + ".o") for src in SOURCES]
+        cmds = [[cc, *HIPCC_FLAGS, *extra_flags, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(src), "-o", str(obj)]
+                for src, obj in zip(SOURCES, objects)]
+        jobs = max(1, min(len(cmds), os.cpu_count() or 1))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for cmd in cmds]:
+                f.result()
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objects), "-o", str(tmp)], verbose)
     os.replace(tmp, output)
     return output
 

@@ -1,0 +1,8 @@
+// kernels_f16.hip -- launch table of the scan kernels with a, b and h stored as f16.
+#include "instances.hpp"
+
+namespace linrec_host {
+
+const Launch* pick_launch_f16(const TileShape& s) { return pick_launch<linrec::F16>(s); }
+
+}  // namespace linrec_host

@@ -1,0 +1,8 @@
+// kernels_f32.hip -- launch table of the scan kernels with a, b and h stored as f32.
+#include "instances.hpp"
+
+namespace linrec_host {
+
+const Launch* pick_launch_f32(const TileShape& s) { return pick_launch<float>(s); }
+
+}  // namespace linrec_host

@@ -1,0 +1,49 @@
+// launch.hpp -- host-side description of one kernel instantiation: the tile
+// shape a call asks for and the table entry that launches the matching
+// template instance.  The instances for each storage type live in their own
+// translation unit (kernels_f32.hip, kernels_bf16.hip, kernels_f16.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_kernel.hpp"
+
+namespace linrec_host {
+
+struct TileShape {
+    int vec;  // channels per lane
+    int t;    // positions per lane
+    int w;    // data waves per workgroup
+    int p;    // most lanes that share one position of a channel slab (power of two <= 64)
+    int q;    // persistent workgroups per CU (0: as many as fit)
+    int m;    // 0: persistent workgroups with carry waves; 1: one tile per workgroup
+};
+
+// Instantiated tile shapes.  Persistent workgroups keep two register buffers
+// of T positions x VEC channels, which spill at VEC = 4, T = 16; 15 data waves
+// leave at most 128 registers a lane, which spill when VEC * T > 16.
+inline bool tile_supported(const TileShape& s) {
+    const bool vec_ok = s.vec == 1 || s.vec == 4;
+    const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
+    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8 || s.w == 15;
+    const bool m_ok = s.m == 0 || s.m == 1;
+    const bool fits = !(s.m == 0 && s.vec == 4 && s.t == 16) && !(s.w == 15 && s.vec * s.t > 16);
+    const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
+    const bool q_ok = s.q >= 0 && s.q <= 64;
+    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok;
+}
+
+struct Launch {
+    const void* kernel;   // identifies the instantiation (occupancy cache key)
+    void (*run)(dim3 grid, dim3 block, const void* a, const void* b, void* h, const linrec::Geometry&,
+                linrec::WorkspaceHeader*, uint64_t*, hipStream_t);
+    hipError_t (*occupancy)(int* groups_per_cu, int threads);
+};
+
+// Table lookups, one per storage type; nullptr when the shape has no instance.
+const Launch* pick_launch_f32(const TileShape& s);
+const Launch* pick_launch_bf16(const TileShape& s);
+const Launch* pick_launch_f16(const TileShape& s);
+
+}  // namespace linrec_host

@@ -2,26 +2,45 @@
 // tile choice, the per-device lookback workspace and the kernel launch.
 //
 // The operation and its evaluation order are described in scan_kernel.hpp and
-// in the header; this file holds no arithmetic of the recurrence.
+// in the header; this file holds no arithmetic of the recurrence.  The kernel
+// instances live in kernels_f32.hip, kernels_bf16.hip and kernels_f16.hip.
 #include "linrec.h"
-#include "scan_kernel.hpp"
+#include "launch.hpp"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
-#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
 #include <string>
 #include <tuple>
 
+// Zero-fill used to (re)initialise a workspace; a kernel rather than a memset
+// so that it can sit inside captured graphs.
+__global__ void linrec_fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t k = i; k < n; k += step) p[k] = 0u;
+}
+
+// A scan over zero positions leaves the state unchanged: h_final = h_init (or 0).
+__global__ void linrec_pass_state(const float* __restrict__ h_init, float* __restrict__ h_final, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    for (int64_t k = i; k < n; k += step) h_final[k] = h_init != nullptr ? h_init[k] : 0.0f;
+}
+
 namespace {
 
 using linrec::Geometry;
 using linrec::WorkspaceHeader;
+using linrec_host::Launch;
+using linrec_host::TileShape;
+using linrec_host::tile_supported;
 
 thread_local std::string t_last_error;
 
@@ -34,36 +53,11 @@ std::string hip_text(hipError_t e) { return std::string(hipGetErrorName(e)) + ":
 
 // ----------------------------------------------------------------------------- tile shapes
 
-struct TileShape {
-    int vec;  // channels per lane
-    int t;    // steps per lane
-    int w;    // waves per workgroup
-    int p;    // most lanes that share one time step of a channel slab (power of two <= 64)
-    int q;    // persistent workgroups per CU (0: as many as fit)
-    int m;    // 0: persistent workgroups with carry waves; 1: one tile per workgroup
-};
-
-bool tile_supported(const TileShape& s) {
-    const bool vec_ok = s.vec == 1 || s.vec == 4;
-    const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
-    // w data waves plus the carry wave make up a workgroup
-    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 6 || s.w == 7 || s.w == 8 || s.w == 14 || s.w == 15;
-    const bool m_ok = s.m == 0 || s.m == 1;
-    // two register buffers of 16 steps x 4 channels do not fit the registers a
-    // lane gets once the workgroup may hold up to 4 carry waves (they spill)
-    const bool fits = !(s.m == 0 && s.vec == 4 && s.t == 16) &&
-                      // 14 or 15 data waves leave at most 128 registers a lane
-                      !(s.w >= 14 && s.vec * s.t > 16);
-    const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
-    const bool q_ok = s.q >= 0 && s.q <= 64;
-    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok;
-}
-
 // Tile choice, from sweeps on MI355X over the five workloads: persistent
-// workgroups of 8 data waves, 4 steps per lane and 32 lanes (512 bytes) per
-// row segment stream best when there are many (batch row, channel slab)
-// sequences.  With few sequences each carry chain is long: one workgroup per
-// tile, 15 data waves and a single carry wave (64-channel slabs) then keep
+// workgroups of 8 data waves, 4 positions per lane and 32 lanes (512 bytes of
+// fp32) per row segment stream best when there are many (batch row, channel
+// slab) sequences.  With few sequences each carry chain is long: one workgroup
+// per tile, 15 data waves and a single carry wave (64-channel slabs) then keep
 // more tiles in flight along each chain.
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
     const int vec = vec4 ? 4 : 1;
@@ -115,9 +109,9 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         pos = end + 1;
     }
     if (!tile_supported(s)) {
-        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,6,7,8,14,15}, vec in {1,4}, "
+        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,15}, vec in {1,4}, "
               "p a power of two <= 64, q in [0, 64], m in {0,1}; not vec=4 with t=16 and m=0, "
-              "not w >= 14 with vec*t > 16)";
+              "not w=15 with vec*t > 16)";
         return false;
     }
     return true;
@@ -135,7 +129,96 @@ uint32_t spin_limit() {
     return 512u;
 }
 
-// ----------------------------------------------------------------------------- geometry
+// ----------------------------------------------------------------------------- the problem
+
+bool checked_mul(int64_t x, int64_t y, int64_t& out) {
+    if (x == 0 || y == 0) { out = 0; return true; }
+    if (x < 0 || y < 0 || x > INT64_MAX / y) return false;
+    out = x * y;
+    return true;
+}
+
+bool checked_add(int64_t x, int64_t y, int64_t& out) {
+    if (x < 0 || y < 0 || x > INT64_MAX - y) return false;
+    out = x + y;
+    return true;
+}
+
+int element_bytes(int32_t dtype) { return dtype == LINREC_F32 ? 4 : 2; }
+
+// Bytes from an operand's first element to one past the last element its
+// strides reach (0 for an empty problem); false on overflow.
+bool operand_extent(const linrec_operand& o, int64_t B, int64_t L, int64_t D, int es, int64_t& bytes) {
+    if (B == 0 || L == 0 || D == 0) { bytes = 0; return true; }
+    int64_t rb = 0, rl = 0, last = 0, n = 0;
+    return checked_mul(B - 1, o.stride_b, rb) && checked_mul(L - 1, o.stride_l, rl) && checked_add(rb, rl, last) &&
+           checked_add(last, D, n) && checked_mul(n, es, bytes);
+}
+
+// h's rows (i, t) of D elements are pairwise disjoint: taking the batch and
+// time dimensions in increasing stride, each stride must clear everything the
+// smaller ones span.
+bool rows_disjoint(const linrec_operand& h, int64_t B, int64_t L, int64_t D) {
+    struct Dim { int64_t stride, count; };
+    Dim dims[2] = {{h.stride_b, B}, {h.stride_l, L}};
+    if (dims[1].stride < dims[0].stride) std::swap(dims[0], dims[1]);
+    int64_t span = D;   // elements spanned by one row and the smaller dimensions so far
+    for (const Dim& d : dims) {
+        if (d.count <= 1) continue;
+        if (d.stride < span) return false;
+        int64_t reach = 0;
+        if (!checked_mul(d.count - 1, d.stride, reach) || !checked_add(reach, span, span)) return false;
+    }
+    return true;
+}
+
+struct Problem {
+    linrec_scan_desc desc;   // strides normalised: unused ones set to harmless values
+    int es;                  // bytes per element
+    int64_t extent_a, extent_b, extent_h;
+    bool vec4;               // 4-channel accesses possible
+};
+
+linrec_status make_problem(const linrec_scan_desc* d, Problem& p) {
+    if (d == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "desc is null");
+    p.desc = *d;
+    linrec_scan_desc& q = p.desc;
+    if (q.B < 0 || q.L < 0 || q.D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
+    if (q.dtype != LINREC_F32 && q.dtype != LINREC_BF16 && q.dtype != LINREC_F16)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "dtype must be LINREC_F32, LINREC_BF16 or LINREC_F16");
+    if (q.reverse != 0 && q.reverse != 1) return fail(LINREC_ERR_INVALID_ARGUMENT, "reverse must be 0 or 1");
+    linrec_operand* ops[3] = {&q.a, &q.b, &q.h};
+    for (linrec_operand* o : ops)
+        if (o->stride_b < 0 || o->stride_l < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "strides must be >= 0");
+    // a stride along a dimension of extent 1 is never used; normalise it so
+    // that the kernels' range arithmetic holds (time strides of h >= D)
+    for (linrec_operand* o : ops) {
+        if (q.B <= 1) o->stride_b = 0;
+        if (q.L <= 1) o->stride_l = q.D;
+    }
+    p.es = element_bytes(q.dtype);
+    int64_t n = 0, bl = 0;
+    if (!checked_mul(q.B, q.L, bl) || !checked_mul(bl, q.D, n) || n > INT64_MAX / 8)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D elements overflow");
+    if (!operand_extent(q.a, q.B, q.L, q.D, p.es, p.extent_a) || !operand_extent(q.b, q.B, q.L, q.D, p.es, p.extent_b) ||
+        !operand_extent(q.h, q.B, q.L, q.D, p.es, p.extent_h))
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "an operand's strides reach beyond 2^63 bytes");
+    if (n > 0 && !rows_disjoint(q.h, q.B, q.L, q.D))
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "the strides of h make rows (i, t) overlap one another");
+    for (linrec_operand* o : ops)
+        if (reinterpret_cast<uintptr_t>(o->ptr) % static_cast<uintptr_t>(p.es) != 0)
+            return fail(LINREC_ERR_INVALID_ARGUMENT, "a, b and h must be aligned to their element size");
+    if (reinterpret_cast<uintptr_t>(q.h_init) % alignof(float) != 0 ||
+        reinterpret_cast<uintptr_t>(q.h_final) % alignof(float) != 0)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "h_init and h_final must be aligned to 4 bytes");
+    const uintptr_t align = static_cast<uintptr_t>(4 * p.es) - 1;
+    bool vec4 = q.D % 4 == 0;
+    for (linrec_operand* o : ops)
+        vec4 = vec4 && (reinterpret_cast<uintptr_t>(o->ptr) & align) == 0 && o->stride_b % 4 == 0 &&
+               o->stride_l % 4 == 0;
+    p.vec4 = vec4;
+    return LINREC_OK;
+}
 
 struct Plan {
     TileShape tile;
@@ -144,38 +227,34 @@ struct Plan {
     size_t workspace_bytes;
 };
 
-bool checked_mul(int64_t x, int64_t y, int64_t& out) {
-    if (x == 0 || y == 0) { out = 0; return true; }
-    if (x > INT64_MAX / y) return false;
-    out = x * y;
-    return true;
-}
-
-linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p) {
-    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
-    int64_t bl = 0, n = 0;
-    if (!checked_mul(B, L, bl) || !checked_mul(bl, D, n) || n > INT64_MAX / 8)
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
-
-    TileShape s = default_tile(B, L, D, aligned16 && D % 4 == 0);
+linrec_status make_plan(const Problem& pr, Plan& p) {
+    const linrec_scan_desc& q = pr.desc;
+    TileShape s = default_tile(q.B, q.L, q.D, pr.vec4);
     if (!tile_supported(s)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
     std::string err;
     if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
-    if (s.vec == 4 && !(aligned16 && D % 4 == 0))
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "vec=4 needs D % 4 == 0 and 16-byte aligned buffers");
+    if (s.vec == 4 && !pr.vec4)
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "vec=4 needs D % 4 == 0, strides that are multiples of 4 and "
+                                                 "operands aligned to 4 elements");
 
     p = Plan{};
     p.tile = s;
     Geometry& g = p.geom;
-    g.L = L;
-    g.D = D;
+    g.L = q.L;
+    g.D = q.D;
+    g.a_sb = q.a.stride_b; g.a_sl = q.a.stride_l;
+    g.b_sb = q.b.stride_b; g.b_sl = q.b.stride_l;
+    g.h_sb = q.h.stride_b; g.h_sl = q.h.stride_l;
+    g.h_init = q.h_init;
+    g.h_final = q.h_final;
+    g.reverse = q.reverse;
     g.spin_limit = spin_limit();
-    if (n == 0) {
+    if (q.B == 0 || q.L == 0 || q.D == 0) {
         p.tiles = 0;
         p.workspace_bytes = 0;
         return LINREC_OK;
     }
-    const int64_t quads = (D + s.vec - 1) / s.vec;
+    const int64_t quads = (q.D + s.vec - 1) / s.vec;
     int lanes = 1, log2_lanes = 0;
     while (lanes < s.p && lanes < quads) { lanes <<= 1; ++log2_lanes; }
     g.lanes_d = lanes;
@@ -187,15 +266,22 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
         return fail(LINREC_ERR_INVALID_ARGUMENT, "the tile needs more than 1024 threads per workgroup (data waves w "
                                                  "plus one carry wave per 64 slab channels); pick a smaller w or p");
     g.nslab = static_cast<int32_t>((quads + lanes - 1) / lanes);
-    g.nseq = B * g.nslab;
+    g.nseq = q.B * g.nslab;
     g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
-    g.nchunks = (L + g.steps_per_tile - 1) / g.steps_per_tile;
+    g.nchunks = (q.L + g.steps_per_tile - 1) / g.steps_per_tile;
     int64_t tiles = 0;
     if (!checked_mul(g.nseq, g.nchunks, tiles) || tiles > 0x7fffffffLL)
         return fail(LINREC_ERR_INVALID_ARGUMENT, "problem needs more than 2^31 - 1 tiles; pick a larger tile (LINREC_TILE)");
-    // a lane addresses its tile through a buffer descriptor with a 31-bit range
-    if (g.steps_per_tile * D * 4 > linrec::kMaxRange)
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "one tile's rows span more than 2 GiB; pick a smaller tile (LINREC_TILE)");
+    // a lane addresses its tile of each operand through a buffer descriptor
+    // with 32-bit offsets; out-of-range offsets stay out of range only while a
+    // tile spans less than kMaxTileBytes
+    for (const linrec_operand* o : {&q.a, &q.b, &q.h}) {
+        int64_t reach = 0, bytes = 0;
+        if (!checked_mul(g.steps_per_tile, o->stride_l, reach) || !checked_add(reach, q.D, reach) ||
+            !checked_mul(reach, pr.es, bytes) || bytes >= linrec::kMaxTileBytes)
+            return fail(LINREC_ERR_INVALID_ARGUMENT, "one tile of an operand spans 1 GiB or more; pick a smaller "
+                                                     "tile (LINREC_TILE)");
+    }
     p.tiles = tiles;
     g.ntiles = tiles;
     if (g.nchunks > 1) {
@@ -209,82 +295,25 @@ linrec_status make_plan(int64_t B, int64_t L, int64_t D, bool aligned16, Plan& p
     return LINREC_OK;
 }
 
-// ----------------------------------------------------------------------------- launch table
-
-struct Launch {
-    const void* kernel;   // identifies the instantiation (occupancy cache key)
-    void (*run)(dim3 grid, dim3 block, const float*, const float*, float*, const Geometry&, WorkspaceHeader*,
-                uint64_t*, hipStream_t);
-    hipError_t (*occupancy)(int* groups_per_cu, int threads);
-};
-
-template <int VEC, int T, int W>
-void run_tiles(dim3 grid, dim3 block, const float* a, const float* b, float* h, const Geometry& g,
-               WorkspaceHeader* hdr, uint64_t* stat, hipStream_t stream) {
-    hipLaunchKernelGGL((linrec::scan_tiles<VEC, T, W>), grid, block, 0, stream, a, b, h, g, hdr, stat);
+void fill_plan(const Plan& p, linrec_plan* plan) {
+    plan->vec = p.tile.vec;
+    plan->steps_per_lane = p.tile.t;
+    plan->waves = p.tile.w;
+    plan->lanes_per_row = p.tiles ? p.geom.lanes_d : 0;
+    plan->steps_per_tile = p.tiles ? p.geom.steps_per_tile : 0;
+    plan->chunks = p.tiles ? p.geom.nchunks : 0;
+    plan->tiles = p.tiles;
+    plan->workspace_bytes = p.workspace_bytes;
+    plan->mode = p.tile.m;
 }
 
-template <int VEC, int T, int W>
-hipError_t occupancy_of(int* groups_per_cu, int threads) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups_per_cu, linrec::scan_tiles<VEC, T, W>, threads, 0);
-}
-
-template <int VEC, int T, int W>
-void run_one(dim3 grid, dim3 block, const float* a, const float* b, float* h, const Geometry& g,
-             WorkspaceHeader* hdr, uint64_t* stat, hipStream_t stream) {
-    hipLaunchKernelGGL((linrec::scan_one<VEC, T, W>), grid, block, 0, stream, a, b, h, g, hdr, stat);
-}
-
-template <int VEC, int T, int W>
-hipError_t occupancy_one(int* groups_per_cu, int threads) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups_per_cu, linrec::scan_one<VEC, T, W>, threads, 0);
-}
-
-template <int VEC, int T, int W>
-const Launch* launch_entry(int mode) {
-    if (mode == 1) {
-        static const Launch one{reinterpret_cast<const void*>(&linrec::scan_one<VEC, T, W>), &run_one<VEC, T, W>,
-                                &occupancy_one<VEC, T, W>};
-        return &one;
-    }
-    if constexpr (VEC == 4 && T == 16) {
-        return nullptr;   // two such register buffers spill
-    } else {
-        static const Launch persistent{reinterpret_cast<const void*>(&linrec::scan_tiles<VEC, T, W>),
-                                       &run_tiles<VEC, T, W>, &occupancy_of<VEC, T, W>};
-        return &persistent;
-    }
-}
-
-using LaunchFn = const Launch*;
-
-template <int VEC, int T>
-LaunchFn pick_w(int w, int m) {
-    switch (w) {
-        case 1: return launch_entry<VEC, T, 1>(m);
-        case 2: return launch_entry<VEC, T, 2>(m);
-        case 4: return launch_entry<VEC, T, 4>(m);
-        case 6: return launch_entry<VEC, T, 6>(m);
-        case 7: return launch_entry<VEC, T, 7>(m);
-        case 8: return launch_entry<VEC, T, 8>(m);
-        case 14: return launch_entry<VEC, T, 14>(m);
-        case 15: return launch_entry<VEC, T, 15>(m);
+const Launch* pick_launch(int32_t dtype, const TileShape& s) {
+    switch (dtype) {
+        case LINREC_F32: return linrec_host::pick_launch_f32(s);
+        case LINREC_BF16: return linrec_host::pick_launch_bf16(s);
+        case LINREC_F16: return linrec_host::pick_launch_f16(s);
         default: return nullptr;
     }
-}
-
-template <int VEC>
-LaunchFn pick_t(int t, int w, int m) {
-    switch (t) {
-        case 4: return pick_w<VEC, 4>(w, m);
-        case 8: return pick_w<VEC, 8>(w, m);
-        case 16: return pick_w<VEC, 16>(w, m);
-        default: return nullptr;
-    }
-}
-
-LaunchFn pick_launch(const TileShape& s) {
-    return s.vec == 4 ? pick_t<4>(s.t, s.w, s.m) : pick_t<1>(s.t, s.w, s.m);
 }
 
 // ----------------------------------------------------------------------------- persistent grid
@@ -340,11 +369,15 @@ struct DeviceWorkspace {
 std::mutex g_mutex;
 std::map<int, DeviceWorkspace> g_workspaces;
 
+unsigned grid_for(int64_t n) {
+    const int64_t blocks = (n + 255) / 256;
+    return static_cast<unsigned>(blocks < 1 ? 1 : (blocks > 4096 ? 4096 : blocks));
+}
+
 linrec_status zero_fill(void* p, size_t bytes, hipStream_t stream) {
     const int64_t words = static_cast<int64_t>(bytes / sizeof(uint32_t));
-    const int64_t blocks64 = (words + 255) / 256;
-    const unsigned blocks = static_cast<unsigned>(blocks64 < 4096 ? (blocks64 < 1 ? 1 : blocks64) : 4096);
-    hipLaunchKernelGGL(linrec::fill_zero_u32, dim3(blocks), dim3(256), 0, stream, static_cast<uint32_t*>(p), words);
+    hipLaunchKernelGGL(linrec_fill_zero_u32, dim3(grid_for(words)), dim3(256), 0, stream, static_cast<uint32_t*>(p),
+                       words);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "workspace clear failed: " + hip_text(e));
     return LINREC_OK;
@@ -391,7 +424,7 @@ linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, voi
 
 // ----------------------------------------------------------------------------- argument checks
 
-linrec_status check_buffer(const void* p, size_t bytes, int device, const char* name) {
+linrec_status check_buffer(const void* p, int64_t bytes, int device, const char* name) {
     hipPointerAttribute_t attr;
     std::memset(&attr, 0, sizeof(attr));
     hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -413,63 +446,59 @@ linrec_status check_buffer(const void* p, size_t bytes, int device, const char* 
     }
     const uintptr_t lo = reinterpret_cast<uintptr_t>(base);
     const uintptr_t at = reinterpret_cast<uintptr_t>(p);
-    if (at < lo || at - lo > size || size - (at - lo) < bytes)
-        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " holds fewer than B*L*D floats");
+    if (at < lo || at - lo > size || size - (at - lo) < static_cast<size_t>(bytes))
+        return fail(LINREC_ERR_INVALID_ARGUMENT, std::string(name) + " reaches beyond its allocation");
     return LINREC_OK;
 }
 
-bool overlaps(const void* x, const void* y, size_t bytes) {
+bool overlaps(const void* x, int64_t xbytes, const void* y, int64_t ybytes) {
+    if (x == nullptr || y == nullptr || xbytes == 0 || ybytes == 0) return false;
     const uintptr_t a = reinterpret_cast<uintptr_t>(x), b = reinterpret_cast<uintptr_t>(y);
-    return a < b + bytes && b < a + bytes;
+    return a < b + static_cast<uintptr_t>(ybytes) && b < a + static_cast<uintptr_t>(xbytes);
 }
 
-}  // namespace
-
-// ============================================================================= C ABI
-
-extern "C" {
-
-linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan* plan) {
-    if (plan == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "plan is null");
-    Plan p;
-    const linrec_status s = make_plan(B, L, D, aligned16 != 0, p);
-    if (s != LINREC_OK) return s;
-    plan->vec = p.tile.vec;
-    plan->steps_per_lane = p.tile.t;
-    plan->waves = p.tile.w;
-    plan->lanes_per_row = p.tiles ? p.geom.lanes_d : 0;
-    plan->steps_per_tile = p.tiles ? p.geom.steps_per_tile : 0;
-    plan->chunks = p.tiles ? p.geom.nchunks : 0;
-    plan->tiles = p.tiles;
-    plan->workspace_bytes = p.workspace_bytes;
-    plan->mode = p.tile.m;
-    return LINREC_OK;
-}
-
-linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D, void* stream) {
-    t_last_error.clear();
-    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
-    if (B == 0 || L == 0 || D == 0) return LINREC_OK;
-    if (a == nullptr || b == nullptr || h == nullptr)
+linrec_status run_scan(const Problem& pr, void* stream) {
+    const linrec_scan_desc& q = pr.desc;
+    const int64_t states = q.B * q.D;
+    const int64_t state_bytes = states * static_cast<int64_t>(sizeof(float));
+    const bool empty = q.B == 0 || q.L == 0 || q.D == 0;
+    if (empty && (states == 0 || q.h_final == nullptr)) return LINREC_OK;
+    if (!empty && (q.a.ptr == nullptr || q.b.ptr == nullptr || q.h.ptr == nullptr))
         return fail(LINREC_ERR_INVALID_ARGUMENT, "a, b and h must be non-null when B*L*D > 0");
-
-    const bool aligned16 = ((reinterpret_cast<uintptr_t>(a) | reinterpret_cast<uintptr_t>(b) |
-                             reinterpret_cast<uintptr_t>(h)) & 15u) == 0;
-    Plan p;
-    linrec_status s = make_plan(B, L, D, aligned16, p);
-    if (s != LINREC_OK) return s;
-    const size_t bytes = static_cast<size_t>(B * L * D) * sizeof(float);
-    if (overlaps(h, a, bytes) || overlaps(h, b, bytes))
+    // written buffers overlap nothing else; a, b and h_init may overlap each other
+    if (overlaps(q.h.ptr, pr.extent_h, q.a.ptr, pr.extent_a) || overlaps(q.h.ptr, pr.extent_h, q.b.ptr, pr.extent_b))
         return fail(LINREC_ERR_OVERLAP, "h overlaps a or b");
+    if (overlaps(q.h_init, state_bytes, q.h.ptr, pr.extent_h))
+        return fail(LINREC_ERR_OVERLAP, "h_init overlaps h");
+    if (overlaps(q.h_final, state_bytes, q.a.ptr, pr.extent_a) || overlaps(q.h_final, state_bytes, q.b.ptr, pr.extent_b) ||
+        overlaps(q.h_final, state_bytes, q.h.ptr, pr.extent_h) || overlaps(q.h_final, state_bytes, q.h_init, state_bytes))
+        return fail(LINREC_ERR_OVERLAP, "h_final overlaps another buffer");
+
+    Plan p;
+    linrec_status s = make_plan(pr, p);
+    if (s != LINREC_OK) return s;
 
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: " + hip_text(e));
-    if ((s = check_buffer(a, bytes, device, "a")) != LINREC_OK) return s;
-    if ((s = check_buffer(b, bytes, device, "b")) != LINREC_OK) return s;
-    if ((s = check_buffer(h, bytes, device, "h")) != LINREC_OK) return s;
+    if (!empty) {
+        if ((s = check_buffer(q.a.ptr, pr.extent_a, device, "a")) != LINREC_OK) return s;
+        if ((s = check_buffer(q.b.ptr, pr.extent_b, device, "b")) != LINREC_OK) return s;
+        if ((s = check_buffer(q.h.ptr, pr.extent_h, device, "h")) != LINREC_OK) return s;
+    }
+    if (q.h_init != nullptr && (s = check_buffer(q.h_init, state_bytes, device, "h_init")) != LINREC_OK) return s;
+    if (q.h_final != nullptr && (s = check_buffer(q.h_final, state_bytes, device, "h_final")) != LINREC_OK) return s;
 
     const hipStream_t hs = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    if (empty) {
+        // only L == 0 with B*D > 0 and an h_final reaches here: the state passes through
+        hipLaunchKernelGGL(linrec_pass_state, dim3(grid_for(states)), dim3(256), 0, hs, q.h_init, q.h_final, states);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
+        return LINREC_OK;
+    }
+
     void* ws = nullptr;
     if (p.workspace_bytes > 0) {
         s = acquire_workspace(device, p.workspace_bytes, hs, ws);
@@ -480,41 +509,109 @@ linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, i
                                                       linrec::kDoneBytes)
                         : nullptr;
 
-    const LaunchFn fn = pick_launch(p.tile);
+    const Launch* fn = pick_launch(q.dtype, p.tile);
     if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
-    if (p.tile.m == 1) {
-        // one tile per workgroup; the hardware keeps as many resident as fit
-        (void)hipGetLastError();
-        fn->run(dim3(static_cast<uint32_t>(p.tiles)), dim3((p.tile.w + p.geom.carry_waves) * linrec::kWave), a, b, h,
-                p.geom, hdr, stat, hs);
-        e = hipGetLastError();
-        if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
-        return LINREC_OK;
-    }
     const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
-    int64_t resident = 0;
-    if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
-    // persistent workgroups: as many as fit at once (or fewer, per LINREC_TILE's
-    // q = workgroups per CU), never more than there are tiles
-    int64_t groups = resident;
-    if (p.tile.q > 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
-            groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);
+    int64_t groups = p.tiles;   // one tile per workgroup
+    if (p.tile.m == 0) {
+        // persistent workgroups: as many as fit at once (or fewer, per
+        // LINREC_TILE's q = workgroups per CU), never more than there are tiles
+        int64_t resident = 0;
+        if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
+        groups = resident;
+        if (p.tile.q > 0) {
+            int cus = 0;
+            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
+                groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);
+        }
+        groups = std::min<int64_t>(groups, p.tiles);
     }
-    groups = std::min<int64_t>(groups, p.tiles);
     (void)hipGetLastError();
-    fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), a, b, h, p.geom, hdr, stat, hs);
+    fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), q.a.ptr, q.b.ptr, const_cast<void*>(q.h.ptr), p.geom,
+            hdr, stat, hs);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));
     return LINREC_OK;
+}
+
+// linrec_scan's operands as a descriptor: contiguous fp32 (B, L, D), forward.
+linrec_scan_desc contiguous_f32(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D) {
+    linrec_scan_desc d;
+    std::memset(&d, 0, sizeof(d));
+    d.B = B;
+    d.L = L;
+    d.D = D;
+    d.dtype = LINREC_F32;
+    d.reverse = 0;
+    const int64_t sl = D, sb = L * D;   // callers have checked that B*L*D does not overflow
+    d.a = linrec_operand{a, sb, sl};
+    d.b = linrec_operand{b, sb, sl};
+    d.h = linrec_operand{h, sb, sl};
+    return d;
+}
+
+bool size_ok(int64_t B, int64_t L, int64_t D) {
+    int64_t bl = 0, n = 0;
+    return B >= 0 && L >= 0 && D >= 0 && checked_mul(B, L, bl) && checked_mul(bl, D, n) && n <= INT64_MAX / 8;
+}
+
+}  // namespace
+
+// ============================================================================= C ABI
+
+extern "C" {
+
+linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan* plan) {
+    if (plan == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "plan is null");
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0 and B*L*D*4 bytes fit");
+    // stand-in addresses with the alignment asked about; nothing is dereferenced
+    const float* base = reinterpret_cast<const float*>(aligned16 ? uintptr_t(256) : uintptr_t(260));
+    const linrec_scan_desc d = contiguous_f32(base, base, const_cast<float*>(base), B, L, D);
+    Problem pr;
+    linrec_status s = make_problem(&d, pr);
+    if (s != LINREC_OK) return s;
+    Plan p;
+    if ((s = make_plan(pr, p)) != LINREC_OK) return s;
+    fill_plan(p, plan);
+    return LINREC_OK;
+}
+
+linrec_status linrec_scan_ex_plan(const linrec_scan_desc* desc, linrec_plan* plan) {
+    if (plan == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "plan is null");
+    Problem pr;
+    linrec_status s = make_problem(desc, pr);
+    if (s != LINREC_OK) return s;
+    Plan p;
+    if ((s = make_plan(pr, p)) != LINREC_OK) return s;
+    fill_plan(p, plan);
+    return LINREC_OK;
+}
+
+linrec_status linrec_scan_ex(const linrec_scan_desc* desc, void* stream) {
+    t_last_error.clear();
+    Problem pr;
+    const linrec_status s = make_problem(desc, pr);
+    if (s != LINREC_OK) return s;
+    return run_scan(pr, stream);
+}
+
+linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D, void* stream) {
+    t_last_error.clear();
+    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
+    if (B == 0 || L == 0 || D == 0) return LINREC_OK;
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
+    const linrec_scan_desc d = contiguous_f32(a, b, h, B, L, D);
+    Problem pr;
+    const linrec_status s = make_problem(&d, pr);
+    if (s != LINREC_OK) return s;
+    return run_scan(pr, stream);
 }
 
 const char* linrec_status_string(int status) {
     switch (status) {
         case LINREC_OK: return "success";
         case LINREC_ERR_INVALID_ARGUMENT: return "invalid argument";
-        case LINREC_ERR_OVERLAP: return "output overlaps an input";
+        case LINREC_ERR_OVERLAP: return "output overlaps another buffer";
         case LINREC_ERR_HIP: return "HIP runtime error";
         case LINREC_ERR_OUT_OF_MEMORY: return "out of device memory";
         default: return "unknown status";

@@ -1,34 +1,42 @@
-// scan_kernel.hpp -- gfx950 kernel of the channel-wise linear-recurrence scan.
+// scan_kernel.hpp -- gfx950 kernels of the channel-wise linear-recurrence scan.
 //
 // The recurrence h_t = a_t * h_{t-1} + b_t (h_0 = b_0) runs independently in
-// every (batch row, channel) pair of a (B, L, D) fp32 tensor with D contiguous
+// every (batch row, channel) pair of a (B, L, D) tensor with D contiguous
 // (problem statement of the POPCORNBENCH "Kimi-K2.6 l1_p9" transcript).  Each
 // step is the affine map x -> a_t*x + b_t; applying (a1,b1) and then (a2,b2)
 // is the pair (a2*a1, a2*b1 + b2), identity (1,0) (operator derivation in that
 // transcript's first reasoning block), so any stretch of time steps reduces to
 // one pair and only the running h has to cross a stretch boundary (its
-// running-carry passage).  The kernel is built on that:
+// running-carry passage).  The kernels are built on that:
 //
-//   tile     (batch row, channel slab, time chunk): SC channels x W*G*T steps.
-//   lane     owns VEC consecutive channels (VEC = 4: 128-bit loads along D) and
-//            T consecutive time steps, held in registers.
-//   wave     64 lanes = G groups of P lanes along t; the P lanes of a group
-//            cover the slab's SC = P*VEC channels, so one wave instruction
-//            reads G row segments of P*VEC*4 bytes.
-//   workgroup persistent: W data waves and ceil(SC/64) carry waves take tiles
-//            blockIdx, blockIdx + grid, ... in order; while the carry wave
-//            looks back for one tile, the data waves' loads of the next tile
-//            are already in flight (two register buffers).
-//   steps    (1) load a, b for the lane's T steps ((0, 0) past L or D);
+//   order    the scan runs over positions tau = 0 .. L-1; forward, tau is the
+//            time step t; in reverse (h_t = a_t * h_{t+1} + b_t), t = L-1-tau.
+//            The state before tau = 0 is zero, or h_init when given (then the
+//            first step uses its a); h_final receives the state after tau = L-1.
+//   tile     (batch row, channel slab, chunk of positions): SC channels x
+//            W*G*T positions.
+//   lane     owns VEC consecutive channels (VEC = 4: 128-bit fp32 or 64-bit
+//            16-bit accesses along D) and T consecutive positions, in registers.
+//   wave     64 lanes = G groups of P lanes along tau; the P lanes of a group
+//            cover the slab's SC = P*VEC channels.
+//   workgroup either persistent (scan_tiles: W data waves and ceil(SC/64)
+//            carry waves take tiles blockIdx, blockIdx + grid, ... in order,
+//            the next tile's loads in flight while the current one waits for
+//            its carry) or one per tile (scan_one).
+//   steps    (1) load a, b for the lane's T positions;
 //            (2) per-lane sequential composition -> the lane's pair;
 //            (3) exclusive scan of the G group pairs across the wave;
-//            (4) wave pairs -> LDS -> per-wave exclusive prefix and, per
-//                channel, the tile pair;
+//            (4) wave pairs -> LDS -> per channel, the tile pair;
 //            (5) cross-workgroup carry by decoupled lookback in the carry wave,
 //                one channel per lane: publish the tile pair, read the status
 //                of the next K predecessors in one round trip, fold their pairs
 //                until one has published its inclusive state, publish ours;
-//            (6) replay h = fma(a_t, h, b_t) from the carried-in state, store.
+//            (6) the carry wave turns the wave pairs into the state entering
+//                each wave; replay h = fma(a, h, b) from it, store.
+//
+// Memory: a, b and h each have their own element strides between batch rows
+// and between time steps (the channel stride is 1) and one storage type S
+// (fp32, bf16 or fp16); all arithmetic is fp32.
 //
 // Status words are self-validating 64-bit values: the high half is a tag
 // (call epoch << 2 | kind), the low half the fp32 payload, stored and loaded
@@ -47,7 +55,7 @@ namespace linrec {
 constexpr int kWave = 64;
 constexpr int kLookbackWindow = 4;        // predecessors read per round trip
 constexpr uint32_t kKindAggregate = 1u;   // payload: one component of the tile pair
-constexpr uint32_t kKindInclusive = 2u;   // payload: state h at the tile's last step
+constexpr uint32_t kKindInclusive = 2u;   // payload: state after the tile's last position
 
 // Workspace: a header, kDoneSlots slot lines (128 bytes each: word 0 counts
 // the workgroups of the current call that hold the epoch, word 1 is the epoch
@@ -72,10 +80,15 @@ constexpr size_t kDoneBytes = size_t(kDoneSlots) * kLineWords * sizeof(uint32_t)
 struct Geometry {
     int64_t L, D;
     int64_t nseq;          // B * nslab
-    int64_t nchunks;       // time chunks per sequence
+    int64_t nchunks;       // chunks of positions per sequence
     int64_t steps_per_tile;
     int64_t ntiles;        // nseq * nchunks
     int64_t nstatus;       // entries per status array (ntiles * SC)
+    int64_t a_sb, a_sl;    // element strides of a between batch rows and time steps
+    int64_t b_sb, b_sl;
+    int64_t h_sb, h_sl;    // h_sl >= D whenever L > 1 (h rows never overlap)
+    const float* h_init;   // (B, D) fp32, the state before position 0; null: zero
+    float* h_final;        // (B, D) fp32, receives the state after position L-1; may be null
     int32_t nslab;         // channel slabs per batch row
     int32_t lanes_d;       // P, power of two <= 64
     int32_t log2_lanes_d;
@@ -83,6 +96,7 @@ struct Geometry {
     int32_t slab_channels; // SC = P * VEC
     int32_t carry_waves;   // ceil(SC / 64): one slab channel per carry-wave lane
     uint32_t spin_limit;   // polls of one predecessor before recomputing its pair
+    int32_t reverse;       // 0: position tau is time step tau; 1: time step L-1-tau
 };
 
 template <int VEC> struct Vec { float v[VEC]; };
@@ -94,47 +108,105 @@ template <int VEC> __device__ __forceinline__ Vec<VEC> splat(float x) {
     return r;
 }
 
+// ---------------------------------------------------------------------------
+// Storage types.  a, b and h are fp32, bf16 or fp16 in memory; values widen to
+// fp32 on load and round to nearest even on store.
+struct Bf16 { uint16_t bits; };
+struct F16 { uint16_t bits; };
+
+template <typename S> constexpr int storage_bytes() { return sizeof(S) == 4 ? 4 : 2; }
+
+__device__ __forceinline__ float widen_bits(Bf16, uint32_t h) { return __uint_as_float(h << 16); }
+__device__ __forceinline__ float widen_bits(F16, uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+__device__ __forceinline__ uint32_t narrow_bits(Bf16, float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ uint32_t narrow_bits(F16, float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+}
+
+// Value of element p (plain load; used off the streaming path).
+__device__ __forceinline__ float load_one(const float* p) { return *p; }
+__device__ __forceinline__ float load_one(const Bf16* p) { return widen_bits(Bf16{}, p->bits); }
+__device__ __forceinline__ float load_one(const F16* p) { return widen_bits(F16{}, p->bits); }
+
 // Streaming accesses of a, b and h go through buffer resources: each tile
-// gets a descriptor whose range ends with its batch row, so a load past the
-// end of the sequence returns 0 and a store past it is dropped by the
-// hardware.  The loops therefore have no branches, which lets the compiler
+// gets a descriptor per operand whose range ends with the tile's last valid
+// element, so a load outside it returns 0 and a store outside it is dropped by
+// the hardware.  The loops therefore have no branches, which lets the compiler
 // wait only for the loads a step needs instead of everything in flight.  The
 // accesses are nontemporal (every byte is touched once); on gfx950 that
 // measured 10-20% faster than plain accesses for this pattern.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBufferConfig = 0x00020000;   // descriptor word 3 for gfx9-family raw buffers
 constexpr int kNontemporal = 2;             // cache-policy bit: no temporal reuse expected
 constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset beyond every tile's range
 constexpr int64_t kMaxRange = 0x7fffffff;      // largest range one descriptor is given
+// Largest byte span the host lets one tile of an operand cover.  Below 2^30,
+// every offset a lane forms stays outside its tile's range whenever it should:
+// kOutOfRange moved by up to a tile's span either way (reverse scans step
+// backwards, as wrapping 32-bit offsets), and a negative offset before the
+// range start, both land at or above 2^30, beyond any range.
+constexpr int64_t kMaxTileBytes = int64_t(1) << 30;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_range(const float* base, int64_t bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_range(const void* base, int64_t bytes) {
     const int64_t n = bytes < kMaxRange ? bytes : kMaxRange;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, static_cast<int>(n), kBufferConfig);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(n), kBufferConfig);
 }
 
-template <int VEC> __device__ __forceinline__ Vec<VEC> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+template <typename S, int VEC>
+__device__ __forceinline__ Vec<VEC> load_vec(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     Vec<VEC> x;
-    if constexpr (VEC == 4) {
-        const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNontemporal);
-        x.v[0] = __uint_as_float(t.x); x.v[1] = __uint_as_float(t.y);
-        x.v[2] = __uint_as_float(t.z); x.v[3] = __uint_as_float(t.w);
-    } else {
+    if constexpr (storage_bytes<S>() == 4) {
+        if constexpr (VEC == 4) {
+            const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kNontemporal);
+            x.v[0] = __uint_as_float(t.x); x.v[1] = __uint_as_float(t.y);
+            x.v[2] = __uint_as_float(t.z); x.v[3] = __uint_as_float(t.w);
+        } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i)
-            x.v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, kNontemporal));
+            for (int i = 0; i < VEC; ++i)
+                x.v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, kNontemporal));
+        }
+    } else {
+        if constexpr (VEC == 4) {
+            const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNontemporal);
+            x.v[0] = widen_bits(S{}, t.x & 0xffffu); x.v[1] = widen_bits(S{}, t.x >> 16);
+            x.v[2] = widen_bits(S{}, t.y & 0xffffu); x.v[3] = widen_bits(S{}, t.y >> 16);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                x.v[i] = widen_bits(S{}, __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * i, 0, kNontemporal));
+        }
     }
     return x;
 }
 
-template <int VEC> __device__ __forceinline__ void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const Vec<VEC>& x) {
-    if constexpr (VEC == 4) {
-        const u32x4 t = {__float_as_uint(x.v[0]), __float_as_uint(x.v[1]), __float_as_uint(x.v[2]),
-                         __float_as_uint(x.v[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNontemporal);
-    } else {
+template <typename S, int VEC>
+__device__ __forceinline__ void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off, const Vec<VEC>& x) {
+    if constexpr (storage_bytes<S>() == 4) {
+        if constexpr (VEC == 4) {
+            const u32x4 t = {__float_as_uint(x.v[0]), __float_as_uint(x.v[1]), __float_as_uint(x.v[2]),
+                             __float_as_uint(x.v[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(t, r, off, 0, kNontemporal);
+        } else {
 #pragma unroll
-        for (int i = 0; i < VEC; ++i)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.v[i]), r, off + 4 * i, 0, kNontemporal);
+            for (int i = 0; i < VEC; ++i)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x.v[i]), r, off + 4 * i, 0, kNontemporal);
+        }
+    } else {
+        if constexpr (VEC == 4) {
+            const u32x2 t = {narrow_bits(S{}, x.v[0]) | (narrow_bits(S{}, x.v[1]) << 16),
+                             narrow_bits(S{}, x.v[2]) | (narrow_bits(S{}, x.v[3]) << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(t, r, off, 0, kNontemporal);
+        } else {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i)
+                __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(narrow_bits(S{}, x.v[i])), r,
+                                                      off + 2 * i, 0, kNontemporal);
+        }
     }
 }
 
@@ -187,20 +259,56 @@ __device__ __forceinline__ uint32_t observe32(const uint32_t* p) {
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return static_cast<uint32_t>(w >> 32); }
 __device__ __forceinline__ float payload_of(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
 
+// Time step of scan position tau.
+__device__ __forceinline__ int64_t time_of(const Geometry& g, int64_t tau) { return g.reverse ? g.L - 1 - tau : tau; }
+
+// State before position 0 for channel d of batch row `row`.
+__device__ __forceinline__ float initial_state(const Geometry& g, int64_t row, int64_t d) {
+    return g.h_init != nullptr ? g.h_init[row * g.D + d] : 0.0f;
+}
+
+// One operand's view of a tile: descriptor, this lane's first offset and the
+// offset step between consecutive positions (negative, as a wrapping 32-bit
+// value, when the scan runs backwards in memory).
+struct OperandSpot {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t off;
+    uint32_t step;
+};
+
 // Where one tile sits and what this lane covers of it.
 struct TileSpot {
     int64_t chunk, seq, row, slab;
-    int64_t t0;     // first time step of this lane
+    int64_t tau0;   // first position of this lane
     bool d_ok;      // this lane's channels exist
-    __amdgpu_buffer_rsrc_t ra, rb, rh;   // the tile's rows up to the end of its batch row
-    uint32_t off;   // byte offset of this lane's first element (kOutOfRange if d_ok is false)
-    uint32_t step;  // bytes between consecutive time steps (D * 4)
+    OperandSpot a, b, h;
 };
 
-__device__ __forceinline__ TileSpot locate(const float* a, const float* b, float* h, const Geometry& g, int64_t tile,
+// The tile covers positions [first, end) of its sequence, end <= L, i.e. time
+// steps [t_lo, t_lo + span) with span = end - first.  The descriptor starts at
+// time step t_lo of the batch row and its range ends with the element
+// (t_lo + span - 1, D - 1).  A position past L is, forward, a time step past
+// the range's end (time strides of h are >= D), and in reverse a step before
+// t_lo, whose negative offset wraps beyond 2^31 > any range; channels past D
+// get kOutOfRange.  So such loads read 0 and such stores are dropped.
+template <typename S>
+__device__ __forceinline__ OperandSpot operand_spot(const S* base, int64_t sb, int64_t sl, const Geometry& g,
+                                                    int64_t row, int64_t t_lo, int64_t span, int64_t lane_rel,
+                                                    int64_t d0, bool d_ok) {
+    constexpr int64_t es = storage_bytes<S>();
+    OperandSpot o;
+    const int64_t bytes = ((span - 1) * sl + g.D) * es;
+    o.r = make_range(base + row * sb + t_lo * sl, bytes);
+    o.off = d_ok ? static_cast<uint32_t>((lane_rel * sl + d0) * es) : kOutOfRange;
+    o.step = static_cast<uint32_t>((g.reverse ? -sl : sl) * es);
+    return o;
+}
+
+template <typename S>
+__device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const Geometry& g, int64_t tile,
                                            int wave, int quad, int grp, int vec, int T) {
     TileSpot s;
-    // time chunk is the slow index: a tile's predecessors come before it in
+    // the chunk is the slow index: a tile's predecessors come before it in
     // every workgroup's order, and the tiles in flight spread over all sequences
     s.chunk = tile / g.nseq;
     s.seq = tile - s.chunk * g.nseq;
@@ -208,47 +316,49 @@ __device__ __forceinline__ TileSpot locate(const float* a, const float* b, float
     s.slab = s.seq - s.row * g.nslab;
     const int64_t d0 = s.slab * g.slab_channels + static_cast<int64_t>(quad) * vec;
     s.d_ok = d0 < g.D;
-    const int64_t first = s.chunk * g.steps_per_tile;                // first time step of the tile
+    const int64_t first = s.chunk * g.steps_per_tile;
+    const int64_t end = first + g.steps_per_tile < g.L ? first + g.steps_per_tile : g.L;
     const int64_t local = static_cast<int64_t>(wave * g.groups + grp) * T;
-    s.t0 = first + local;
-    const int64_t origin = (s.row * g.L + first) * g.D;                // element (row, first, 0)
-    const int64_t bytes = (g.L - first) * g.D * 4;                     // to the end of the batch row
-    s.ra = make_range(a + origin, bytes);
-    s.rb = make_range(b + origin, bytes);
-    s.rh = make_range(h + origin, bytes);
-    s.off = s.d_ok ? static_cast<uint32_t>((local * g.D + d0) * 4) : kOutOfRange;
-    s.step = static_cast<uint32_t>(g.D * 4);
+    s.tau0 = first + local;
+    const int64_t span = end - first;
+    // time step of the range start, and this lane's first time step relative to it
+    const int64_t t_lo = g.reverse ? g.L - end : first;
+    const int64_t rel = g.reverse ? span - 1 - local : local;
+    s.a = operand_spot<S>(a, g.a_sb, g.a_sl, g, s.row, t_lo, span, rel, d0, s.d_ok);
+    s.b = operand_spot<S>(b, g.b_sb, g.b_sl, g, s.row, t_lo, span, rel, d0, s.d_ok);
+    s.h = operand_spot<S>(h, g.h_sb, g.h_sl, g, s.row, t_lo, span, rel, d0, s.d_ok);
     return s;
 }
 
-// (1) loads of one tile into a register buffer.  Steps past the end of the
-// sequence and channels past D read as (a, b) = (0, 0): such steps come after
-// every real step of their lane, group and wave, and their channels are never
-// stored, so no stored output depends on them.
-template <int VEC, int T>
+// (1) loads of one tile into a register buffer.  Positions past L and channels
+// past D read as (a, b) = (0, 0) (or, for a or b whose time stride is below D,
+// other in-bounds elements): such positions come after every real position of
+// their lane, group and wave, and their channels are never stored, so no
+// stored output depends on them.
+template <typename S, int VEC, int T>
 __device__ __forceinline__ void load_tile(Vec<VEC> (&av)[T], Vec<VEC> (&bv)[T], const TileSpot& s) {
 #pragma unroll
     for (int j = 0; j < T; ++j) {
-        av[j] = load_vec<VEC>(s.ra, s.off + j * s.step);
-        bv[j] = load_vec<VEC>(s.rb, s.off + j * s.step);
+        av[j] = load_vec<S, VEC>(s.a.r, s.a.off + j * s.a.step);
+        bv[j] = load_vec<S, VEC>(s.b.r, s.b.off + j * s.b.step);
     }
 }
 
-// The pair of time chunk j for one channel, composed directly from a and b:
-// the fallback when chunk j's tile has published nothing for a while.  It only
+// The pair of chunk j for one channel, composed directly from a and b: the
+// fallback when chunk j's tile has published nothing for a while.  It only
 // reads inputs, so it always finishes.
-__device__ inline void chunk_pair_from_inputs(const float* __restrict__ a, const float* __restrict__ b,
-                                              const Geometry& g, int64_t row, int64_t d, int64_t j,
-                                              float& A, float& Bv) {
+template <typename S>
+__device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
+                                              int64_t row, int64_t d, int64_t j, float& A, float& Bv) {
     A = 1.0f;
     Bv = 0.0f;
-    const int64_t t_begin = j * g.steps_per_tile;
-    const int64_t t_end = t_begin + g.steps_per_tile < g.L ? t_begin + g.steps_per_tile : g.L;
-    const float* pa = a + (row * g.L + t_begin) * g.D + d;
-    const float* pb = b + (row * g.L + t_begin) * g.D + d;
-    for (int64_t t = t_begin; t < t_end; ++t, pa += g.D, pb += g.D) {
-        const float at = t == 0 ? 0.0f : *pa;
-        Bv = __builtin_fmaf(at, Bv, *pb);
+    const int64_t tau_begin = j * g.steps_per_tile;
+    const int64_t tau_end = tau_begin + g.steps_per_tile < g.L ? tau_begin + g.steps_per_tile : g.L;
+    for (int64_t tau = tau_begin; tau < tau_end; ++tau) {
+        const int64_t t = time_of(g, tau);
+        const float at = (tau == 0 && g.h_init == nullptr) ? 0.0f : load_one(a + row * g.a_sb + t * g.a_sl + d);
+        const float bt = load_one(b + row * g.b_sb + t * g.b_sl + d);
+        Bv = __builtin_fmaf(at, Bv, bt);
         A = at * A;
     }
 }
@@ -258,12 +368,13 @@ __device__ inline void chunk_pair_from_inputs(const float* __restrict__ a, const
 // their pairs, nearest first, until one of them has published its inclusive
 // state.  A predecessor that shows nothing within spin_limit polls has its pair
 // recomputed from the inputs (`recomputed` is set).  Returns the state that
-// enters the tile.
-__device__ inline float lookback_channel(const float* __restrict__ a, const float* __restrict__ b,
-                                         const Geometry& g, int64_t row, int64_t d,
-                                         const uint64_t* __restrict__ stat_a, const uint64_t* __restrict__ stat_b,
-                                         const uint64_t* __restrict__ stat_p, int64_t idx, int64_t chunk,
-                                         uint32_t tag_agg, uint32_t tag_inc, bool& recomputed) {
+// enters the tile; h0 is the state before position 0.
+template <typename S>
+__device__ inline float lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
+                                         int64_t row, int64_t d, float h0, const uint64_t* __restrict__ stat_a,
+                                         const uint64_t* __restrict__ stat_b, const uint64_t* __restrict__ stat_p,
+                                         int64_t idx, int64_t chunk, uint32_t tag_agg, uint32_t tag_inc,
+                                         bool& recomputed) {
     const int64_t stride = g.slab_channels;   // status distance between consecutive chunks
     float acc_a = 1.0f, acc_b = 0.0f;
     int64_t j = chunk - 1;                    // nearest predecessor not folded yet
@@ -308,15 +419,15 @@ __device__ inline float lookback_channel(const float* __restrict__ a, const floa
         }
         // predecessor j shows nothing: compose its pair from the inputs
         float pa, pb;
-        chunk_pair_from_inputs(a, b, g, row, d, j, pa, pb);
+        chunk_pair_from_inputs<S>(a, b, g, row, d, j, pa, pb);
         acc_b = __builtin_fmaf(acc_a, pb, acc_b);
         acc_a = acc_a * pa;
         recomputed = true;
         --j;
         spins = 0;
     }
-    // walked past chunk 0 through recomputed pairs: the state before t = 0 is zero
-    return acc_b;
+    // walked past chunk 0 through recomputed pairs: apply them to the state before position 0
+    return __builtin_fmaf(acc_a, h0, acc_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -380,35 +491,50 @@ __device__ inline void count_done(WorkspaceHeader* hdr, uint32_t epoch, uint32_t
     }
 }
 
-// LDS shared by the waves of one workgroup.
+// LDS shared by the waves of one workgroup.  Between the two barriers of a
+// tile, (agg_a, agg_b)[w] hold data wave w's pair; after the second barrier
+// agg_a[w] holds the state entering wave w's positions (the carry wave
+// rewrites it in place).  Each data wave reads and writes only its own slot.
 template <int VEC, int W>
 struct TileShared {
-    Vec<VEC> agg_a[W][kWave];   // pair of each data wave's steps, per lane channel group
+    Vec<VEC> agg_a[W][kWave];   // per data wave and lane channel group
     Vec<VEC> agg_b[W][kWave];
-    float h_in[kWave * VEC];    // state entering the tile, per slab channel
 };
 
 // What a lane keeps of its tile between the scan in registers and the store.
 template <int VEC>
 struct LanePrefix {
-    Vec<VEC> ex_a, ex_b;   // pair of the steps before this lane's in its wave (group scan)
+    Vec<VEC> ex_a, ex_b;   // pair of the positions before this lane's in its wave (group scan)
 };
 
 // Steps (2)-(4) up to the hand-over: per-lane composition, the group scan
-// along t inside the wave, and the wave's pair into LDS.  Inputs at t = 0 get
-// a = 0: the state before t = 0 is zero, so a_0 never contributes.
+// along tau inside the wave, and the wave's pair into LDS.  Without h_init the
+// state before position 0 is zero, so that position's a never contributes: use
+// 0 for it.
 template <int VEC, int T, int W>
 __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, TileShared<VEC, W>& sh, const TileSpot& s,
                                                           int lane, int wave, int quad, int grp, Vec<VEC> (&av)[T],
-                                                          const Vec<VEC> (&bv)[T]) {
-    if (s.t0 == 0) av[0] = splat<VEC>(0.0f);
+                                                          Vec<VEC> (&bv)[T]) {
+    if (s.tau0 == 0 && g.h_init == nullptr) av[0] = splat<VEC>(0.0f);
+    if (g.h_final != nullptr) {
+        // positions past L become identity steps (1, 0): they then leave the
+        // state of position L-1 unchanged to the end of its lane (no stored
+        // output depends on them either way)
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            if (s.tau0 + j >= g.L) {
+                av[j] = splat<VEC>(1.0f);
+                bv[j] = splat<VEC>(0.0f);
+            }
+        }
+    }
 
-    // (2) per-lane sequential composition over the T steps
+    // (2) per-lane sequential composition over the T positions
     Vec<VEC> la = av[0], lb = bv[0];
 #pragma unroll
     for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, av[j], bv[j]);
 
-    // (3) groups along t inside the wave: inclusive scan, then shift to exclusive
+    // (3) groups along tau inside the wave: inclusive scan, then shift to exclusive
     LanePrefix<VEC> pre;
     pre.ex_a = splat<VEC>(1.0f);
     pre.ex_b = splat<VEC>(0.0f);
@@ -438,108 +564,114 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
     return pre;
 }
 
-// (4) after the hand-over barrier: the pair of the waves before this one.
-template <int VEC, int W>
-__device__ __forceinline__ void wave_prefix(TileShared<VEC, W>& sh, int wave, int quad, Vec<VEC>& pw_a, Vec<VEC>& pw_b) {
-    pw_a = splat<VEC>(1.0f);
-    pw_b = splat<VEC>(0.0f);
-    for (int v = 0; v < wave; ++v) then_apply<VEC>(pw_a, pw_b, sh.agg_a[v][quad], sh.agg_b[v][quad]);
-}
-
 // (6) once the state entering the tile is in LDS: the state entering this
-// lane's steps, then replay and store.  Stores past the end of the sequence
-// or of the channels are dropped.
-template <int VEC, int T, int W>
-__device__ __forceinline__ void replay_store(const TileShared<VEC, W>& sh, const TileSpot& s, int quad,
-                                             const LanePrefix<VEC>& pre, const Vec<VEC>& pw_a, const Vec<VEC>& pw_b,
-                                             const Vec<VEC> (&av)[T], const Vec<VEC> (&bv)[T]) {
-    Vec<VEC> hs;
+// lane's positions, then replay and store.  Stores past L or D are dropped.
+// When h_final is wanted, positions past L were made identity steps (see
+// scan_registers), so the lane holding position L-1 ends its replay on the
+// state there and writes it out.
+template <typename S, int VEC, int T, int W>
+__device__ __forceinline__ void replay_store(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
+                                             int wave, int quad, const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
+                                             const Vec<VEC> (&bv)[T]) {
+    Vec<VEC> hs = sh.agg_a[wave][quad];   // state entering this wave's positions
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-        hs.v[i] = sh.h_in[quad * VEC + i];
-        hs.v[i] = __builtin_fmaf(pw_a.v[i], hs.v[i], pw_b.v[i]);
-        hs.v[i] = __builtin_fmaf(pre.ex_a.v[i], hs.v[i], pre.ex_b.v[i]);
-    }
+    for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(pre.ex_a.v[i], hs.v[i], pre.ex_b.v[i]);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
 #pragma unroll
         for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(av[j].v[i], hs.v[i], bv[j].v[i]);
-        store_vec<VEC>(s.rh, s.off + j * s.step, hs);
+        store_vec<S, VEC>(s.h.r, s.h.off + j * s.h.step, hs);
+    }
+    if (g.h_final != nullptr && s.d_ok && s.tau0 <= g.L - 1 && g.L - 1 < s.tau0 + T) {
+        float* out = g.h_final + s.row * g.D + s.slab * g.slab_channels + quad * VEC;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) out[i] = hs.v[i];
     }
 }
 
 // (5) for slab channel c of the tile (one per lane; the caller has passed the
 // hand-over barrier): fold the data waves' pairs into the tile pair, publish
 // it, look back for the state entering the tile, publish the state leaving
-// it, and put the entering state into LDS.
-template <int VEC, int W>
-__device__ __forceinline__ void carry_channel(const float* __restrict__ a, const float* __restrict__ b,
-                                              const Geometry& g, uint64_t* __restrict__ stat, TileShared<VEC, W>& sh,
-                                              int c, uint32_t epoch, bool& recomputed, int64_t tile) {
+// it, and replace each data wave's pair in LDS by the state entering that
+// wave's positions.
+template <typename S, int VEC, int W>
+__device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
+                                              uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
+                                              uint32_t epoch, bool& recomputed, int64_t tile) {
     if (c >= g.slab_channels) return;
     const int64_t chunk = tile / g.nseq;
     const int64_t seq = tile - chunk * g.nseq;
     const int64_t row = seq / g.nslab;
     const int64_t slab = seq - row * g.nslab;
     const int64_t d = slab * g.slab_channels + c;
+    float* agg_a = &sh.agg_a[0][0].v[0];
+    const float* agg_b = &sh.agg_b[0][0].v[0];
     float h_in = 0.0f;
-    if (g.nchunks > 1 && d < g.D) {
-        const bool has_successor = chunk + 1 < g.nchunks;
-        const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
-        const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
-        uint64_t* stat_a = stat;
-        uint64_t* stat_b = stat + g.nstatus;
-        uint64_t* stat_p = stat + 2 * g.nstatus;
-        const float* agg_a = &sh.agg_a[0][0].v[0];
-        const float* agg_b = &sh.agg_b[0][0].v[0];
-        float ta = agg_a[c], tb = agg_b[c];
+    if (d < g.D) {
+        const float h0 = initial_state(g, row, d);
+        h_in = h0;
+        if (g.nchunks > 1) {
+            const bool has_successor = chunk + 1 < g.nchunks;
+            const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
+            const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
+            uint64_t* stat_a = stat;
+            uint64_t* stat_b = stat + g.nstatus;
+            uint64_t* stat_p = stat + 2 * g.nstatus;
+            float ta = agg_a[c], tb = agg_b[c];
 #pragma unroll
-        for (int v = 1; v < W; ++v) {
-            const float na = agg_a[v * kWave * VEC + c], nb = agg_b[v * kWave * VEC + c];
-            tb = __builtin_fmaf(na, tb, nb);
-            ta = na * ta;
-        }
-        // status entries are sequence-major: chunk j-1 of a sequence sits
-        // slab_channels entries before chunk j
-        const int64_t idx = (seq * g.nchunks + chunk) * g.slab_channels + c;
-        if (chunk > 0) {
-            if (has_successor) {
-                publish(stat_a + idx, tag_agg, ta);
-                publish(stat_b + idx, tag_agg, tb);
+            for (int v = 1; v < W; ++v) {
+                const float na = agg_a[v * kWave * VEC + c], nb = agg_b[v * kWave * VEC + c];
+                tb = __builtin_fmaf(na, tb, nb);
+                ta = na * ta;
             }
-            h_in = lookback_channel(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc, recomputed);
+            // status entries are sequence-major: chunk j-1 of a sequence sits
+            // slab_channels entries before chunk j
+            const int64_t idx = (seq * g.nchunks + chunk) * g.slab_channels + c;
+            if (chunk > 0) {
+                if (has_successor) {
+                    publish(stat_a + idx, tag_agg, ta);
+                    publish(stat_b + idx, tag_agg, tb);
+                }
+                h_in = lookback_channel<S>(a, b, g, row, d, h0, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc,
+                                           recomputed);
+            }
+            if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
         }
-        if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
     }
-    sh.h_in[c] = h_in;
+    float hv = h_in;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+        const int k = v * kWave * VEC + c;
+        const float na = agg_a[k], nb = agg_b[k];
+        agg_a[k] = hv;
+        hv = __builtin_fmaf(na, hv, nb);
+    }
 }
 
 // Data wave, one tile of the persistent loop: start the loads of the
 // workgroup's next tile into (nav, nbv), scan the tile whose inputs are in
 // (av, bv), hand the wave's pair to the carry wave, and once the carry is in,
 // replay and store.
-template <int VEC, int T, int W>
-__device__ __forceinline__ void data_tile(const float* __restrict__ a, const float* __restrict__ b,
-                                          float* __restrict__ h, const Geometry& g, TileShared<VEC, W>& sh,
-                                          int lane, int wave, int quad, int grp, int64_t tile, Vec<VEC> (&av)[T],
-                                          Vec<VEC> (&bv)[T], int64_t next, Vec<VEC> (&nav)[T], Vec<VEC> (&nbv)[T]) {
+template <typename S, int VEC, int T, int W>
+__device__ __forceinline__ void data_tile(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
+                                          const Geometry& g, TileShared<VEC, W>& sh, int lane, int wave, int quad,
+                                          int grp, int64_t tile, Vec<VEC> (&av)[T], Vec<VEC> (&bv)[T], int64_t next,
+                                          Vec<VEC> (&nav)[T], Vec<VEC> (&nbv)[T]) {
     // (1) the next tile's loads stay in flight while this tile is scanned,
     // waits for its carry and is stored.  They are issued even when there is
     // no next tile (then every lane's offset is out of range and nothing is
     // read), so that every step issues the same memory operations and the
     // compiler can count exactly which loads a step has to wait for.
     {
-        TileSpot ns = locate(a, b, h, g, next < g.ntiles ? next : tile, wave, quad, grp, VEC, T);
-        if (next >= g.ntiles) ns.off = kOutOfRange;
-        load_tile<VEC, T>(nav, nbv, ns);
+        TileSpot ns = locate<S>(a, b, h, g, next < g.ntiles ? next : tile, wave, quad, grp, VEC, T);
+        if (next >= g.ntiles) ns.a.off = ns.b.off = kOutOfRange;
+        load_tile<S, VEC, T>(nav, nbv, ns);
     }
-    const TileSpot s = locate(a, b, h, g, tile, wave, quad, grp, VEC, T);
+    const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
     const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
-    Vec<VEC> pw_a, pw_b;
-    wave_prefix<VEC, W>(sh, wave, quad, pw_a, pw_b);
-    __syncthreads();   // the carry wave has written the state entering the tile
-    replay_store<VEC, T, W>(sh, s, quad, pre, pw_a, pw_b, av, bv);
+    __syncthreads();   // the carry wave has written the states entering the waves
+    replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);
 }
 
 // Most threads a workgroup of W data waves and up to VEC carry waves may have
@@ -551,9 +683,9 @@ constexpr int group_limit(int w, int vec) { return (w + vec) * kWave < 1024 ? (w
 // same number of tiles and meets the same two barriers per tile.  Carry waves
 // issue no data loads or stores, so their status polls never queue behind the
 // data traffic (loads and stores retire in order per wave).
-template <int VEC, int T, int W>
+template <typename S, int VEC, int T, int W>
 __global__ void __launch_bounds__(group_limit(W, VEC))
-scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
+scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
            Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
     __shared__ TileShared<VEC, W> sh;
 
@@ -572,8 +704,8 @@ scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __re
         bool recomputed = false;
         for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride) {
             __syncthreads();   // wave pairs are in LDS
-            carry_channel<VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
-            __syncthreads();   // the state entering the tile is in LDS
+            carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+            __syncthreads();   // the states entering the waves are in LDS
         }
         if (chained && __ballot(recomputed) != 0 && lane == 0)
             __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -588,14 +720,14 @@ scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __re
     Vec<VEC> a0[T], b0[T], a1[T], b1[T];
     int64_t tile = blockIdx.x;
     if (tile >= g.ntiles) return;
-    load_tile<VEC, T>(a0, b0, locate(a, b, h, g, tile, wave, quad, grp, VEC, T));
-    data_tile<VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
+    load_tile<S, VEC, T>(a0, b0, locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T));
+    data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
     tile += stride;
     while (tile < g.ntiles) {
-        data_tile<VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a1, b1, tile + stride, a0, b0);
+        data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a1, b1, tile + stride, a0, b0);
         tile += stride;
         if (tile >= g.ntiles) break;
-        data_tile<VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
+        data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
         tile += stride;
     }
 }
@@ -607,9 +739,9 @@ scan_tiles(const float* __restrict__ a, const float* __restrict__ b, float* __re
 // data waves keeps their register count, and so the number of workgroups
 // resident per CU, down; with many resident, the loads of some overlap the
 // lookback of others.
-template <int VEC, int T, int W>
+template <typename S, int VEC, int T, int W>
 __global__ void __launch_bounds__(group_limit(W, VEC))
-scan_one(const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
+scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
          Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
     __shared__ TileShared<VEC, W> sh;
 
@@ -627,8 +759,8 @@ scan_one(const float* __restrict__ a, const float* __restrict__ b, float* __rest
         }
         bool recomputed = false;
         __syncthreads();   // wave pairs are in LDS
-        carry_channel<VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
-        __syncthreads();   // the state entering the tile is in LDS
+        carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+        __syncthreads();   // the states entering the waves are in LDS
         if (!chained) return;
         if (__ballot(recomputed) != 0 && lane == 0)
             __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -638,23 +770,13 @@ scan_one(const float* __restrict__ a, const float* __restrict__ b, float* __rest
 
     const int quad = lane & (g.lanes_d - 1);
     const int grp = lane >> g.log2_lanes_d;
-    const TileSpot s = locate(a, b, h, g, tile, wave, quad, grp, VEC, T);
+    const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
     Vec<VEC> av[T], bv[T];
-    load_tile<VEC, T>(av, bv, s);
+    load_tile<S, VEC, T>(av, bv, s);
     const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
-    __syncthreads();   // the state entering the tile is in LDS
-    Vec<VEC> pw_a, pw_b;
-    wave_prefix<VEC, W>(sh, wave, quad, pw_a, pw_b);
-    replay_store<VEC, T, W>(sh, s, quad, pre, pw_a, pw_b, av, bv);
-}
-
-// Zero-fill used to (re)initialise a workspace; a kernel rather than a memset
-// so that it can sit inside captured graphs.
-__global__ void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    const int64_t step = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    for (int64_t k = i; k < n; k += step) p[k] = 0u;
+    __syncthreads();   // the states entering the waves are in LDS
+    replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);
 }
 
 }  // namespace linrec

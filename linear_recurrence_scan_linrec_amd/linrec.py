@@ -29,6 +29,8 @@ LINREC_ERR_OUT_OF_MEMORY = 4
 EXPORTED = (
     "linrec_scan",
     "linrec_scan_plan",
+    "linrec_scan_ex",
+    "linrec_scan_ex_plan",
     "linrec_status_string",
     "linrec_last_error_message",
     "linrec_device_timeouts",
@@ -50,6 +52,33 @@ class linrec_plan(ctypes.Structure):
     ]
 
 
+class linrec_operand(ctypes.Structure):
+    _fields_ = [
+        ("ptr", ctypes.c_void_p),
+        ("stride_b", ctypes.c_int64),
+        ("stride_l", ctypes.c_int64),
+    ]
+
+
+class linrec_scan_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64),
+        ("L", ctypes.c_int64),
+        ("D", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("reverse", ctypes.c_int32),
+        ("a", linrec_operand),
+        ("b", linrec_operand),
+        ("h", linrec_operand),
+        ("h_init", ctypes.c_void_p),
+        ("h_final", ctypes.c_void_p),
+    ]
+
+
+LINREC_F32, LINREC_BF16, LINREC_F16 = 0, 1, 2
+DTYPES = {torch.float32: LINREC_F32, torch.bfloat16: LINREC_BF16, torch.float16: LINREC_F16}
+
+
 class LinrecError(RuntimeError):
     """A linrec_* call returned a status other than LINREC_OK."""
 
@@ -68,6 +97,10 @@ def _load() -> ctypes.CDLL:
     lib.linrec_scan.argtypes = [vp, vp, vp, i64, i64, i64, vp]
     lib.linrec_scan_plan.restype = ctypes.c_int
     lib.linrec_scan_plan.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.POINTER(linrec_plan)]
+    lib.linrec_scan_ex.restype = ctypes.c_int
+    lib.linrec_scan_ex.argtypes = [ctypes.POINTER(linrec_scan_desc), vp]
+    lib.linrec_scan_ex_plan.restype = ctypes.c_int
+    lib.linrec_scan_ex_plan.argtypes = [ctypes.POINTER(linrec_scan_desc), ctypes.POINTER(linrec_plan)]
     lib.linrec_status_string.restype = ctypes.c_char_p
     lib.linrec_status_string.argtypes = [ctypes.c_int]
     lib.linrec_last_error_message.restype = ctypes.c_char_p
@@ -105,35 +138,96 @@ def linrec_scan_raw(a_ptr: int, b_ptr: int, h_ptr: int, B: int, L: int, D: int, 
     return _lib.linrec_scan(a_ptr, b_ptr, h_ptr, B, L, D, stream_ptr)
 
 
-def linrec_scan(a, b, h=None, stream=None):
-    """h[i,0,d] = b[i,0,d], h[i,t,d] = a[i,t,d]*h[i,t-1,d] + b[i,t,d] on the GPU.
+def _operand(t) -> linrec_operand:
+    return linrec_operand(t.data_ptr(), t.stride(0), t.stride(1))
 
-    ``a`` and ``b`` are contiguous fp32 CUDA tensors of shape (B, L, D) on one
-    device; ``h`` (optional) receives the result and is allocated when omitted.
-    The call is enqueued on ``stream`` (a ``torch.cuda.Stream``; default: the
-    current stream of a's device) and returns without synchronising.
-    """
-    for name, t in (("a", a), ("b", b)):
-        if not isinstance(t, torch.Tensor):
-            raise TypeError(f"{name} must be a torch.Tensor")
-        if t.dtype != torch.float32 or not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape (B, L, D)")
-    if a.shape != b.shape or a.device != b.device:
-        raise ValueError("a and b must have one shape and one device")
-    if h is None:
-        h = torch.empty_like(a)
-    elif (h.shape != a.shape or h.dtype != torch.float32 or h.device != a.device
-          or not h.is_contiguous()):
-        raise ValueError("h must be a contiguous float32 tensor shaped and placed like a")
+
+def _check_operand(name, t, shape=None, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda or t.dim() != 3:
+        raise ValueError(f"{name} must be a CUDA tensor of shape (B, L, D)")
+    if t.dtype not in DTYPES:
+        raise ValueError(f"{name} must be float32, bfloat16 or float16, not {t.dtype}")
+    if t.shape[2] > 1 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have unit stride along D (the last dimension)")
+    if shape is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device):
+        raise ValueError(f"{name} must be shaped, typed and placed like a: {tuple(shape)} {dtype} {device}")
+
+
+def _check_state(name, t, B, D, device):
+    if t is None:
+        return
+    if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != (B, D)
+            or t.device != device or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape (B, D) = {(B, D)} on {device}")
+
+
+def make_desc(a, b, h, h_init=None, h_final=None, reverse=False) -> linrec_scan_desc:
+    """The linrec_scan_desc for torch tensors (no checks beyond what ctypes needs)."""
     B, L, D = a.shape
+    return linrec_scan_desc(B, L, D, DTYPES[a.dtype], int(bool(reverse)), _operand(a), _operand(b), _operand(h),
+                            None if h_init is None else h_init.data_ptr(),
+                            None if h_final is None else h_final.data_ptr())
+
+
+def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_final=False, reverse=False):
+    """The channel-wise linear recurrence on the GPU.
+
+    Forward (default): h[i,0,d] = a[i,0,d]*h_init[i,d] + b[i,0,d] (h_init taken as 0 when
+    omitted, so h[i,0,d] = b[i,0,d]) and h[i,t,d] = a[i,t,d]*h[i,t-1,d] + b[i,t,d].
+    ``reverse=True`` runs the same recurrence from t = L-1 down to 0 (h[i,t,d] uses h[i,t+1,d]).
+
+    ``a`` and ``b`` are CUDA tensors of shape (B, L, D), one dtype (float32, bfloat16 or
+    float16), unit stride along D and any non-negative strides otherwise (views, expanded or
+    time-major layouts work without copies); arithmetic is fp32.  ``h`` (optional) receives the
+    result in the same dtype and is allocated contiguous when omitted.  ``h_init`` is an
+    optional (B, D) float32 state before the first step; ``h_final`` an optional (B, D) float32
+    tensor that receives the state after the last step (allocated when ``return_final``).
+    Returns ``h``, or ``(h, h_final)`` when a final state is asked for.  The call is enqueued on
+    ``stream`` (default: the current stream of a's device) and returns without synchronising.
+    """
+    _check_operand("a", a)
+    _check_operand("b", b, a.shape, a.dtype, a.device)
+    B, L, D = a.shape
+    if h is None:
+        h = torch.empty((B, L, D), dtype=a.dtype, device=a.device)
+    else:
+        _check_operand("h", h, a.shape, a.dtype, a.device)
+    _check_state("h_init", h_init, B, D, a.device)
+    want_final = return_final or h_final is not None
+    if want_final and h_final is None:
+        h_final = torch.empty((B, D), dtype=torch.float32, device=a.device)
+    _check_state("h_final", h_final, B, D, a.device)
+    plain = (a.dtype == torch.float32 and not reverse and h_init is None and h_final is None
+             and a.is_contiguous() and b.is_contiguous() and h.is_contiguous())
+
+    def call(s):
+        if plain:
+            _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
+        else:
+            desc = make_desc(a, b, h, h_init, h_final, reverse)
+            _check(_lib.linrec_scan_ex(ctypes.byref(desc), s.cuda_stream))
+
     if a.device.index == torch.cuda.current_device():
-        s = torch.cuda.current_stream() if stream is None else stream
-        _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
-        return h
-    with torch.cuda.device(a.device):   # the library works on the current HIP device
-        s = torch.cuda.current_stream(a.device) if stream is None else stream
-        _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
-    return h
+        call(torch.cuda.current_stream() if stream is None else stream)
+    else:
+        with torch.cuda.device(a.device):   # the library works on the current HIP device
+            call(torch.cuda.current_stream(a.device) if stream is None else stream)
+    return (h, h_final) if want_final else h
+
+
+def linrec_scan_ex_raw(desc: linrec_scan_desc, stream_ptr: int = 0) -> int:
+    """Direct C-ABI call of linrec_scan_ex; returns the status code."""
+    return _lib.linrec_scan_ex(ctypes.byref(desc), stream_ptr)
+
+
+def plan_for(a, b, h=None, *, h_init=None, h_final=None, reverse=False) -> dict:
+    """The plan linrec_scan_ex would use for these tensors (host arithmetic only)."""
+    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse)
+    plan = linrec_plan()
+    _check(_lib.linrec_scan_ex_plan(ctypes.byref(desc), ctypes.byref(plan)))
+    return {name: getattr(plan, name) for name, _ in linrec_plan._fields_}
 
 
 def linrec_scan_plan(B: int, L: int, D: int, aligned16: bool = True) -> dict:

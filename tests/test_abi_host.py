@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_status_strings():
     assert binding.linrec_status_string(0) == "success"
-    assert binding.linrec_status_string(2) == "output overlaps an input"
+    assert binding.linrec_status_string(2) == "output overlaps another buffer"
     assert binding.linrec_status_string(99) == "unknown status"
 
 
@@ -126,3 +126,98 @@ def test_tile_override(tile_env):
     os.environ["LINREC_TILE"] = "vec=4"
     with pytest.raises(binding.LinrecError):
         binding.linrec_scan_plan(3, 100, 7)   # vec=4 cannot serve D % 4 != 0
+
+
+# ----------------------------------------------------------------------------- linrec_scan_ex on the host
+
+def desc(B, L, D, dtype=0, reverse=0, base=1 << 32, strides=None, h_init=None, h_final=None):
+    """A linrec_scan_desc over fake, well separated addresses (no kernel runs)."""
+    es = 4 if dtype == 0 else 2
+    n = max(B * L * D, 1)
+    st = strides or [(L * D, D)] * 3
+    ops = [binding.linrec_operand(base + k * 4 * n * es, *st[k]) for k in range(3)]
+    return binding.linrec_scan_desc(B, L, D, dtype, reverse, *ops, h_init, h_final)
+
+
+def ex_plan(d):
+    plan = binding.linrec_plan()
+    status = binding.library().linrec_scan_ex_plan(ctypes.byref(d), ctypes.byref(plan))
+    return status, {name: getattr(plan, name) for name, _ in binding.linrec_plan._fields_}
+
+
+def test_ex_plan_of_contiguous_f32_is_linrec_scan_plan():
+    for shape in ((32, 4096, 256), (2, 262144, 64), (3, 100, 7), (1, 64, 8)):
+        st, p = ex_plan(desc(*shape))
+        assert st == binding.LINREC_OK
+        assert p == binding.linrec_scan_plan(*shape)
+
+
+def test_ex_plan_vector_form_needs_aligned_strides():
+    assert ex_plan(desc(4, 100, 64, dtype=1))[1]["vec"] == 4
+    assert ex_plan(desc(4, 100, 64, dtype=2))[1]["vec"] == 4
+    # a time stride that is not a multiple of 4 elements, or an operand 2 elements in
+    st = [(100 * 66, 66), (100 * 64, 64), (100 * 64, 64)]
+    assert ex_plan(desc(4, 100, 64, strides=st))[1]["vec"] == 1
+    d = desc(4, 100, 64, dtype=1)
+    d.b.ptr += 4
+    assert ex_plan(d)[1]["vec"] == 1
+    # broadcast a over batch rows and time (strides 0) keeps the vector form
+    st = [(0, 0), (100 * 64, 64), (100 * 64, 64)]
+    assert ex_plan(desc(4, 100, 64, strides=st))[1]["vec"] == 4
+
+
+def test_ex_rejects_bad_descriptors():
+    bad = binding.LINREC_ERR_INVALID_ARGUMENT
+    lib = binding.library()
+    assert lib.linrec_scan_ex(None, None) == bad
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, dtype=3)), None) == bad
+    assert "dtype" in binding.linrec_last_error_message()
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, reverse=2)), None) == bad
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, strides=[(128, -16), (128, 16), (128, 16)])), None) == bad
+    assert "strides" in binding.linrec_last_error_message()
+    # rows of h overlap: time stride below D, or batch rows on top of each other
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, strides=[(128, 16), (128, 16), (128, 8)])), None) == bad
+    assert "overlap one another" in binding.linrec_last_error_message()
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, strides=[(128, 16), (128, 16), (64, 16)])), None) == bad
+    # time-major h (batch stride D, time stride B*D) is fine
+    assert ex_plan(desc(2, 8, 16, strides=[(128, 16), (128, 16), (16, 32)]))[0] == binding.LINREC_OK
+    # an operand not aligned to its element size, a state not aligned to 4 bytes
+    d = desc(2, 8, 16, dtype=1)
+    d.a.ptr += 1
+    assert lib.linrec_scan_ex(ctypes.byref(d), None) == bad
+    assert "aligned" in binding.linrec_last_error_message()
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, h_init=(1 << 40) + 2)), None) == bad
+    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, h_final=(1 << 40) + 6)), None) == bad
+    # a time stride so large that one tile would span 1 GiB or more
+    assert ex_plan(desc(2, 8000, 16, strides=[(0, 1 << 22), (128000, 16), (128000, 16)]))[0] == bad
+    assert "1 GiB" in binding.linrec_last_error_message()
+
+
+def test_ex_overlaps_are_rejected_before_any_hip_call():
+    lib = binding.library()
+    over = binding.LINREC_ERR_OVERLAP
+    d = desc(2, 8, 16)
+    d.h.ptr = d.a.ptr + 64
+    assert lib.linrec_scan_ex(ctypes.byref(d), None) == over
+    d = desc(2, 8, 16, h_final=None)
+    d.h_final = d.b.ptr + 4
+    assert lib.linrec_scan_ex(ctypes.byref(d), None) == over
+    d = desc(2, 8, 16)
+    d.h_init = d.h.ptr
+    assert lib.linrec_scan_ex(ctypes.byref(d), None) == over
+    d = desc(2, 8, 16, h_init=1 << 44)
+    d.h_final = d.h_init
+    assert lib.linrec_scan_ex(ctypes.byref(d), None) == over
+    # a and b may alias, and h_init may alias an input
+    d = desc(2, 8, 16)
+    d.b.ptr = d.a.ptr
+    d.h_init = d.a.ptr
+    assert ex_plan(d)[0] == binding.LINREC_OK
+
+
+def test_ex_empty_problems_without_a_final_state_are_noops():
+    lib = binding.library()
+    for shape in ((0, 10, 10), (10, 0, 10), (10, 10, 0)):
+        d = desc(*shape)
+        d.a.ptr = d.b.ptr = d.h.ptr = None
+        assert lib.linrec_scan_ex(ctypes.byref(d), None) == binding.LINREC_OK

@@ -104,10 +104,10 @@ def supported_tiles():
     for m in (0, 1):
         for vec in (1, 4):
             for t in (4, 8, 16):
-                for w in (1, 2, 4, 6, 7, 8, 14, 15):
+                for w in (1, 2, 4, 8, 15):
                     if m == 0 and vec == 4 and t == 16:
                         continue
-                    if w >= 14 and vec * t > 16:
+                    if w == 15 and vec * t > 16:
                         continue
                     out.append((vec, t, w, m))
     return out
