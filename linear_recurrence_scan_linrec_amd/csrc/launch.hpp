@@ -18,6 +18,8 @@ struct TileShape {
     int p;    // most lanes that share one position of a channel slab (power of two <= 64)
     int q;    // persistent workgroups per CU (0: as many as fit)
     int m;    // 0: persistent workgroups with carry waves; 1: one tile per workgroup
+    int l;    // 1: persistent workgroups keep the carry local when their grid can divide
+              // the sequences among them; 0: always look back
 };
 
 // Instantiated tile shapes.  Persistent workgroups keep two register buffers
@@ -31,7 +33,8 @@ inline bool tile_supported(const TileShape& s) {
     const bool fits = !(s.m == 0 && s.vec == 4 && s.t == 16) && !(s.w == 15 && s.vec * s.t > 16);
     const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
     const bool q_ok = s.q >= 0 && s.q <= 64;
-    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok;
+    const bool l_ok = s.l == 0 || s.l == 1;
+    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok && l_ok;
 }
 
 struct Launch {

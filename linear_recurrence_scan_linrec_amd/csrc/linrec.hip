@@ -53,18 +53,47 @@ std::string hip_text(hipError_t e) { return std::string(hipGetErrorName(e)) + ":
 
 // ----------------------------------------------------------------------------- tile shapes
 
-// Tile choice, from sweeps on MI355X over the five workloads: persistent
-// workgroups of 8 data waves, 4 positions per lane and 32 lanes (512 bytes of
-// fp32) per row segment stream best when there are many (batch row, channel
-// slab) sequences.  With few sequences each carry chain is long: one workgroup
-// per tile, 15 data waves and a single carry wave (64-channel slabs) then keep
-// more tiles in flight along each chain.
-TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
+// CUs assumed by the plan entry points, which make no HIP call (MI355X).
+constexpr int kPlanCus = 256;
+
+// Lanes per row segment that make_plan derives from a requested p: the
+// smallest power of two that is >= min(p, channel groups per row).
+int64_t lanes_for(int p, int64_t quads) {
+    int64_t lanes = 1;
+    while (lanes < p && lanes < quads) lanes <<= 1;
+    return lanes;
+}
+
+// Tile choice, from sweeps on MI355X over the five workloads.
+//  - When some slab width gives every CU a (batch row, channel slab) sequence
+//    of its own (1..kMaxLocalSeqs per workgroup), persistent workgroups keep
+//    the carry local: no status words and no cross-workgroup wait.  The widest
+//    such slab up to 32 lanes is taken (wider row segments stream better, but
+//    64-lane slabs need four carry waves and measured slower); 8 positions per
+//    lane; 2 data waves when a wave covers 8 or more row segments, else 4.
+//    (B=32 L=4096 D=256: 8-lane slabs, 76.7 us against 82.5 us looking back;
+//    B=16 L=512 D=8192: 32-lane slabs, 134 us against 146 us with 64 lanes.)
+//  - Otherwise the tiles look back: persistent workgroups of 8 data waves, 4
+//    positions per lane and 32 lanes (512 bytes of fp32) per row segment; with
+//    fewer than 32 sequences each chain is long, and one workgroup per tile,
+//    15 data waves and a single carry wave (64-channel slabs) keep more tiles
+//    in flight along each chain.
+TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus) {
     const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
-    if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0, 0};
-    TileShape s{vec, 4, 8, 32, 0, 0};
-    const int64_t lanes = std::min<int64_t>(32, (D + vec - 1) / vec);
+    if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0, 0, 1};
+    const int64_t quads = (D + vec - 1) / vec;
+    for (int p = 32; p >= 8; p >>= 1) {
+        const int64_t lanes = lanes_for(p, quads);
+        const int64_t nseq = B * ((quads + lanes - 1) / lanes);
+        bool local = false;
+        for (int m = 1; m <= linrec::kMaxLocalSeqs && !local; ++m) local = nseq % m == 0 && nseq / m >= cus;
+        const int w = 64 / lanes >= 8 ? 2 : 4;
+        const int64_t steps = static_cast<int64_t>(w) * (64 / lanes) * 8;
+        if (local && L > steps) return TileShape{vec, 8, w, p, 0, 0, 1};
+    }
+    TileShape s{vec, 4, 8, 32, 0, 0, 1};
+    const int64_t lanes = std::min<int64_t>(32, quads);
     const int64_t sequences = B * ((D + vec * lanes - 1) / (vec * lanes));
     if (sequences < 32) {
         s.m = 1;
@@ -74,7 +103,7 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4) {
     return s;
 }
 
-// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0" (any subset of the keys).
+// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0,l=1" (any subset of the keys).
 bool apply_tile_env(TileShape& s, std::string& err) {
     const char* env = std::getenv("LINREC_TILE");
     if (env == nullptr || *env == '\0') return true;
@@ -102,15 +131,16 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         else if (key == "p") s.p = static_cast<int>(val);
         else if (key == "q") s.q = static_cast<int>(val);
         else if (key == "m") s.m = static_cast<int>(val);
+        else if (key == "l") s.l = static_cast<int>(val);
         else {
-            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q, m";
+            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q, m, l";
             return false;
         }
         pos = end + 1;
     }
     if (!tile_supported(s)) {
         err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,15}, vec in {1,4}, "
-              "p a power of two <= 64, q in [0, 64], m in {0,1}; not vec=4 with t=16 and m=0, "
+              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}; not vec=4 with t=16 and m=0, "
               "not w=15 with vec*t > 16)";
         return false;
     }
@@ -227,9 +257,9 @@ struct Plan {
     size_t workspace_bytes;
 };
 
-linrec_status make_plan(const Problem& pr, Plan& p) {
+linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     const linrec_scan_desc& q = pr.desc;
-    TileShape s = default_tile(q.B, q.L, q.D, pr.vec4);
+    TileShape s = default_tile(q.B, q.L, q.D, pr.vec4, cus);
     if (!tile_supported(s)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
     std::string err;
     if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
@@ -255,8 +285,9 @@ linrec_status make_plan(const Problem& pr, Plan& p) {
         return LINREC_OK;
     }
     const int64_t quads = (q.D + s.vec - 1) / s.vec;
-    int lanes = 1, log2_lanes = 0;
-    while (lanes < s.p && lanes < quads) { lanes <<= 1; ++log2_lanes; }
+    const int lanes = static_cast<int>(lanes_for(s.p, quads));
+    int log2_lanes = 0;
+    while ((1 << log2_lanes) < lanes) ++log2_lanes;
     g.lanes_d = lanes;
     g.log2_lanes_d = log2_lanes;
     g.groups = linrec::kWave / lanes;
@@ -305,6 +336,30 @@ void fill_plan(const Plan& p, linrec_plan* plan) {
     plan->tiles = p.tiles;
     plan->workspace_bytes = p.workspace_bytes;
     plan->mode = p.tile.m;
+}
+
+// Grid of persistent workgroups that keeps the carry local, filling in
+// p.geom.local_seqs, or 0 (local_seqs = 0: the tiles look back).  The grid
+// must divide the (batch row, channel slab) sequences into at most
+// kMaxLocalSeqs per workgroup: workgroup k then takes tiles k, k + grid, ...,
+// which are chunks 0, 1, ... of its own sequences in order, so the state
+// entering each tile is the one its previous tile of that sequence left.  Of
+// the grids with at least one workgroup per CU that fit at once, the smallest
+// is taken (exactly q per CU when LINREC_TILE sets q).  Not with l=0, nor
+// with one chunk per sequence (nothing to carry).
+int64_t local_grid(Plan& p, int64_t resident, int cus) {
+    Geometry& g = p.geom;
+    g.local_seqs = 0;
+    if (p.tile.l == 0 || g.nchunks <= 1) return 0;
+    const int64_t want = p.tile.q > 0 ? static_cast<int64_t>(p.tile.q) * cus : 0;
+    for (int m = linrec::kMaxLocalSeqs; m >= 1; --m) {
+        if (g.nseq % m != 0) continue;
+        const int64_t grid = g.nseq / m;
+        if (grid < cus || grid > resident || (want > 0 && grid != want)) continue;
+        g.local_seqs = m;
+        return grid;
+    }
+    return 0;
 }
 
 const Launch* pick_launch(int32_t dtype, const TileShape& s) {
@@ -474,13 +529,15 @@ linrec_status run_scan(const Problem& pr, void* stream) {
         overlaps(q.h_final, state_bytes, q.h.ptr, pr.extent_h) || overlaps(q.h_final, state_bytes, q.h_init, state_bytes))
         return fail(LINREC_ERR_OVERLAP, "h_final overlaps another buffer");
 
-    Plan p;
-    linrec_status s = make_plan(pr, p);
-    if (s != LINREC_OK) return s;
-
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: " + hip_text(e));
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess || cus < 1) return fail(LINREC_ERR_HIP, "hipDeviceGetAttribute(CU count): " + hip_text(e));
+    Plan p;
+    linrec_status s = make_plan(pr, p, cus);
+    if (s != LINREC_OK) return s;
     if (!empty) {
         if ((s = check_buffer(q.a.ptr, pr.extent_a, device, "a")) != LINREC_OK) return s;
         if ((s = check_buffer(q.b.ptr, pr.extent_b, device, "b")) != LINREC_OK) return s;
@@ -499,8 +556,25 @@ linrec_status run_scan(const Problem& pr, void* stream) {
         return LINREC_OK;
     }
 
+    const Launch* fn = pick_launch(q.dtype, p.tile);
+    if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
+    const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
+    int64_t groups = p.tiles;   // one tile per workgroup
+    if (p.tile.m == 0) {
+        // persistent workgroups: a grid that gives each of them whole
+        // sequences when there is one (the carry then stays local), else as
+        // many as fit at once (or q per CU), never more than there are tiles
+        int64_t resident = 0;
+        if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
+        groups = local_grid(p, resident, cus);
+        if (groups == 0) {
+            groups = resident;
+            if (p.tile.q > 0) groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);
+            groups = std::min<int64_t>(groups, p.tiles);
+        }
+    }
     void* ws = nullptr;
-    if (p.workspace_bytes > 0) {
+    if (p.workspace_bytes > 0 && p.geom.local_seqs == 0) {
         s = acquire_workspace(device, p.workspace_bytes, hs, ws);
         if (s != LINREC_OK) return s;
     }
@@ -508,24 +582,6 @@ linrec_status run_scan(const Problem& pr, void* stream) {
     uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader) +
                                                       linrec::kDoneBytes)
                         : nullptr;
-
-    const Launch* fn = pick_launch(q.dtype, p.tile);
-    if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
-    const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
-    int64_t groups = p.tiles;   // one tile per workgroup
-    if (p.tile.m == 0) {
-        // persistent workgroups: as many as fit at once (or fewer, per
-        // LINREC_TILE's q = workgroups per CU), never more than there are tiles
-        int64_t resident = 0;
-        if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
-        groups = resident;
-        if (p.tile.q > 0) {
-            int cus = 0;
-            if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess && cus > 0)
-                groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);
-        }
-        groups = std::min<int64_t>(groups, p.tiles);
-    }
     (void)hipGetLastError();
     fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), q.a.ptr, q.b.ptr, const_cast<void*>(q.h.ptr), p.geom,
             hdr, stat, hs);
@@ -571,7 +627,7 @@ linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, l
     linrec_status s = make_problem(&d, pr);
     if (s != LINREC_OK) return s;
     Plan p;
-    if ((s = make_plan(pr, p)) != LINREC_OK) return s;
+    if ((s = make_plan(pr, p, kPlanCus)) != LINREC_OK) return s;
     fill_plan(p, plan);
     return LINREC_OK;
 }
@@ -582,7 +638,7 @@ linrec_status linrec_scan_ex_plan(const linrec_scan_desc* desc, linrec_plan* pla
     linrec_status s = make_problem(desc, pr);
     if (s != LINREC_OK) return s;
     Plan p;
-    if ((s = make_plan(pr, p)) != LINREC_OK) return s;
+    if ((s = make_plan(pr, p, kPlanCus)) != LINREC_OK) return s;
     fill_plan(p, plan);
     return LINREC_OK;
 }

@@ -61,6 +61,7 @@ constexpr uint32_t kKindInclusive = 2u;   // payload: state after the tile's las
 // the workgroups of the current call that hold the epoch, word 1 is the epoch
 // of the current call), then three status arrays (pair A, pair B, inclusive
 // state) of nstatus words.
+constexpr int kMaxLocalSeqs = 4;  // sequences one workgroup may carry locally
 constexpr int kLineWords = 32;    // uint32 words per 128-byte line
 constexpr int kDoneSlots = 256;
 
@@ -97,6 +98,10 @@ struct Geometry {
     int32_t carry_waves;   // ceil(SC / 64): one slab channel per carry-wave lane
     uint32_t spin_limit;   // polls of one predecessor before recomputing its pair
     int32_t reverse;       // 0: position tau is time step tau; 1: time step L-1-tau
+    int32_t local_seqs;    // > 0: the persistent grid divides nseq into local_seqs (<= kMaxLocalSeqs)
+                           // sequences per workgroup, so every tile's predecessor was this
+                           // workgroup's own tile local_seqs tiles earlier and the carry stays in
+                           // LDS (no status words, no workspace); 0: decoupled lookback
 };
 
 template <int VEC> struct Vec { float v[VEC]; };
@@ -569,11 +574,11 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
 // When h_final is wanted, positions past L were made identity steps (see
 // scan_registers), so the lane holding position L-1 ends its replay on the
 // state there and writes it out.
-template <typename S, int VEC, int T, int W>
-__device__ __forceinline__ void replay_store(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
-                                             int wave, int quad, const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
-                                             const Vec<VEC> (&bv)[T]) {
-    Vec<VEC> hs = sh.agg_a[wave][quad];   // state entering this wave's positions
+template <typename S, int VEC, int T>
+__device__ __forceinline__ void replay_from(const Geometry& g, Vec<VEC> hs, const TileSpot& s, int quad,
+                                            const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
+                                            const Vec<VEC> (&bv)[T]) {
+    // hs: the state entering this wave's positions
 #pragma unroll
     for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(pre.ex_a.v[i], hs.v[i], pre.ex_b.v[i]);
 #pragma unroll
@@ -582,11 +587,22 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
         for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(av[j].v[i], hs.v[i], bv[j].v[i]);
         store_vec<S, VEC>(s.h.r, s.h.off + j * s.h.step, hs);
     }
-    if (g.h_final != nullptr && s.d_ok && s.tau0 <= g.L - 1 && g.L - 1 < s.tau0 + T) {
-        float* out = g.h_final + s.row * g.D + s.slab * g.slab_channels + quad * VEC;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) out[i] = hs.v[i];
-    }
+    // the state after position L-1, written by the lane that holds it: an
+    // unconditional store whose offset is out of range for every other lane
+    // (and whose range is empty without h_final), so that every replay issues
+    // the same number of memory operations
+    const bool holds_last = g.h_final != nullptr && s.d_ok && s.tau0 <= g.L - 1 && g.L - 1 < s.tau0 + T;
+    const __amdgpu_buffer_rsrc_t fr =
+        make_range(g.h_final != nullptr ? g.h_final + s.row * g.D : nullptr, g.h_final != nullptr ? g.D * 4 : 0);
+    const uint32_t foff = holds_last ? static_cast<uint32_t>((s.slab * g.slab_channels + quad * VEC) * 4) : kOutOfRange;
+    store_vec<float, VEC>(fr, foff, hs);
+}
+
+template <typename S, int VEC, int T, int W>
+__device__ __forceinline__ void replay_store(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
+                                             int wave, int quad, const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
+                                             const Vec<VEC> (&bv)[T]) {
+    replay_from<S, VEC, T>(g, sh.agg_a[wave][quad], s, quad, pre, av, bv);
 }
 
 // (5) for slab channel c of the tile (one per lane; the caller has passed the
@@ -594,10 +610,15 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
 // it, look back for the state entering the tile, publish the state leaving
 // it, and replace each data wave's pair in LDS by the state entering that
 // wave's positions.
+//
+// With a local carry (g.local_seqs > 0), `local` is this channel's LDS cell
+// for the tile's sequence: it holds the state after the workgroup's previous
+// tile of that sequence, which is the state entering this one, and receives
+// the state after this tile.
 template <typename S, int VEC, int W>
 __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
-                                              uint32_t epoch, bool& recomputed, int64_t tile) {
+                                              uint32_t epoch, bool& recomputed, int64_t tile, float* local) {
     if (c >= g.slab_channels) return;
     const int64_t chunk = tile / g.nseq;
     const int64_t seq = tile - chunk * g.nseq;
@@ -610,7 +631,9 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
     if (d < g.D) {
         const float h0 = initial_state(g, row, d);
         h_in = h0;
-        if (g.nchunks > 1) {
+        if (g.local_seqs > 0) {
+            if (chunk > 0) h_in = *local;
+        } else if (g.nchunks > 1) {
             const bool has_successor = chunk + 1 < g.nchunks;
             const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
             const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
@@ -646,7 +669,14 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
         agg_a[k] = hv;
         hv = __builtin_fmaf(na, hv, nb);
     }
+    if (g.local_seqs > 0) *local = hv;
 }
+
+// LDS cells of the local carry: [sequence slot][slab channel].
+template <int VEC>
+struct LocalCarry {
+    float h[kMaxLocalSeqs][kWave * VEC];
+};
 
 // Data wave, one tile of the persistent loop: start the loads of the
 // workgroup's next tile into (nav, nbv), scan the tile whose inputs are in
@@ -691,20 +721,24 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    const bool chained = g.nchunks > 1;
+    const bool chained = g.nchunks > 1 && g.local_seqs == 0;
     const int64_t stride = gridDim.x;
 
     if (wave >= W) {
+        __shared__ LocalCarry<VEC> local;
         const int carry = wave - W;
+        const int c = carry * kWave + lane;
         uint32_t epoch = 0;
         if (chained) {
             epoch = call_epoch(hdr);
             if (carry == 0) count_done(hdr, epoch, count_in(hdr, epoch, lane), lane);
         }
         bool recomputed = false;
+        int slot = 0;   // sequence slot of the local carry: tiles cycle through local_seqs sequences
         for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride) {
             __syncthreads();   // wave pairs are in LDS
-            carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+            carry_channel<S, VEC, W>(a, b, g, stat, sh, c, epoch, recomputed, tile, &local.h[slot][c % (kWave * VEC)]);
+            if (g.local_seqs > 0 && ++slot == g.local_seqs) slot = 0;
             __syncthreads();   // the states entering the waves are in LDS
         }
         if (chained && __ballot(recomputed) != 0 && lane == 0)
@@ -759,7 +793,7 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         }
         bool recomputed = false;
         __syncthreads();   // wave pairs are in LDS
-        carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile);
+        carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile, nullptr);
         __syncthreads();   // the states entering the waves are in LDS
         if (!chained) return;
         if (__ballot(recomputed) != 0 && lane == 0)
@@ -778,5 +812,6 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
     __syncthreads();   // the states entering the waves are in LDS
     replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);
 }
+
 
 }  // namespace linrec

@@ -30,7 +30,7 @@ UNIT_ROUNDOFF = {torch.float32: 0.0, torch.bfloat16: 2.0 ** -8, torch.float16: 2
 
 # tile overrides: the default choice, one tile per workgroup, the 32-bit form, a deep
 # narrow tile, and short tiles with narrow slabs (many chunks, long carry chains)
-TILES = ["", "m=1", "vec=1", "m=1,vec=1,t=8,w=2", "t=8,w=4,p=8", "m=1,t=4,w=1,p=16"]
+TILES = ["", "m=1", "vec=1", "m=1,vec=1,t=8,w=2", "t=8,w=4,p=8", "m=1,t=4,w=1,p=16", "t=4,w=8,p=32,l=0"]
 
 
 @pytest.fixture(scope="module")
@@ -289,3 +289,30 @@ def test_reverse_gives_the_gradient_of_the_forward_scan(lr):
     da = torch.zeros_like(db)
     da[:, 1:] = db[:, 1:] * h[:, :-1]
     check(da, a64.grad.numpy(), torch.float32, "gradient in a")
+
+
+def test_local_carry_with_every_operand_form(lr, tile_env):
+    """Persistent workgroups that keep the carry local (8-lane slabs, one workgroup per CU taking
+    whole sequences), with strided operands, bf16 storage, an initial and a final state, and
+    reverse time."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B, L, D = cus // 8, 1999, 256
+    set_tile("p=8,q=1,w=4,m=0,l=1")
+    a, b, a_np, b_np = device_inputs((B, L, D), 1300, a_lo=0.5, a_hi=1.0)
+    h0_np = np.random.default_rng(1301).standard_normal((B, D)).astype(np.float32)
+    h0 = torch.from_numpy(h0_np).cuda()
+    for reverse in (False, True):
+        fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
+        ref = fn(a_np, b_np, h_init=h0_np)
+        b_tm = b.transpose(0, 1).contiguous().transpose(0, 1)          # time-major b
+        h_big = torch.full((B, L, D + 8), float("nan"), device="cuda")
+        h = h_big[:, :, 4:4 + D]
+        _, hf = lr.linrec_scan(a, b_tm, h, h_init=h0, return_final=True, reverse=reverse)
+        torch.cuda.synchronize()
+        check(h, ref, torch.float32, f"local carry strided reverse={reverse}")
+        check(hf, ref[:, 0 if reverse else -1, :], torch.float32, f"local carry h_final reverse={reverse}")
+        assert torch.isnan(h_big[:, :, :4]).all() and torch.isnan(h_big[:, :, 4 + D:]).all()
+    ab, bb, ab_np, bb_np = device_inputs((B, L, D), 1302, torch.bfloat16, a_lo=0.5, a_hi=1.0)
+    h = lr.linrec_scan(ab, bb)
+    torch.cuda.synchronize()
+    check(h, oracle.linrec_oracle_f64(ab_np, bb_np), torch.bfloat16, "local carry bf16")

@@ -151,10 +151,13 @@ def test_every_tile_shape(lr, tile, tile_env):
 def test_modes_and_grids_alternate_on_one_workspace(lr, tile_env):
     """Consecutive calls with different kernels and grid sizes share the device workspace; each
     call's status words must carry a fresh epoch (a stale word accepted as current would show up
-    as a wrong carry)."""
+    as a wrong carry); calls that keep the carry local in between leave the workspace alone."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     cases = [("m=0", (4, 3000, 256)), ("m=1", (4, 3000, 256)), ("m=1,t=8,w=2", (2, 9000, 64)),
              ("m=0,w=2", (2, 9000, 64)), ("m=1", (4, 3000, 256)), ("m=0", (1, 70000, 8)),
-             ("m=1,p=64,w=8", (3, 5000, 256)), ("m=0", (4, 3000, 256))]
+             ("m=0,p=64,w=8,l=0", (3, 5000, 256)), ("m=1,p=64,w=8", (3, 5000, 256)),
+             ("m=0,p=8,q=1,w=4", (cus // 8, 3000, 256)), ("m=0", (4, 3000, 256)),
+             ("m=0,p=8,q=1,w=2,t=8", (cus // 8, 3100, 256)), ("m=0,w=4,t=8", (2, 9000, 64))]
     for k, (spec, shape) in enumerate(cases):
         os.environ["LINREC_TILE"] = spec
         a, b = li.make_inputs(*shape, seed=500 + k, a_lo=0.9, a_hi=1.0)
@@ -284,3 +287,40 @@ def test_bad_buffers_are_rejected(lr):
     with pytest.raises(ValueError):
         lr.linrec_scan(a.transpose(1, 2), a.transpose(1, 2))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("local", [0, 1])
+def test_local_carry(lr, tile_env, local):
+    """Persistent workgroups whose grid (one per CU here) divides the (batch row, channel slab)
+    sequences into 1, 2 or 4 per workgroup keep the carry in LDS instead of looking back; l=0
+    forces the lookback on the same shapes."""
+    m = 0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for k, (rows, L, D) in enumerate(((cus // 8, 3001, 256), (cus // 4, 1501, 256), (cus // 8, 777, 1024))):
+        os.environ["LINREC_TILE"] = f"p=8,q=1,w=8,m={m},l={local}"
+        a, b = li.make_inputs(rows, L, D, seed=900 + k, a_lo=0.5, a_hi=1.0)
+        plan = lr.linrec_scan_plan(rows, L, D)
+        assert plan["chunks"] > 1 and plan["lanes_per_row"] == 8
+        check_case(lr, a, b, f"local={local} m={m} {(rows, L, D)} sequences={rows * D // 32}")
+
+
+def local_tiles():
+    """(vec, t, w) of every persistent instantiation."""
+    return [(vec, t, w) for vec in (1, 4) for t in (4, 8, 16) for w in (1, 2, 4, 8, 15)
+            if not (vec == 4 and t == 16) and not (w == 15 and vec * t > 16)]
+
+
+@pytest.mark.parametrize("tile", local_tiles(), ids=lambda t: f"vec{t[0]}_t{t[1]}_w{t[2]}")
+def test_every_local_tile_shape(lr, tile_env, tile):
+    """Each persistent instantiation with a local carry, on a ragged shape whose 8-lane slabs give
+    one sequence per CU (so the grid of one workgroup per CU takes whole sequences)."""
+    vec, t, w = tile
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    D = 256 if vec == 4 else 64
+    rows = cus // 8
+    os.environ["LINREC_TILE"] = f"vec={vec},t={t},w={w},p=8,q=1,m=0"
+    for L in (2 * 8 * t * w + 5, 1001):
+        a, b = li.make_inputs(rows, L, D, seed=1200 + vec + t + w + L, a_lo=0.5, a_hi=1.0)
+        plan = lr.linrec_scan_plan(rows, L, D)
+        assert plan["lanes_per_row"] == 8 and plan["vec"] == vec
+        check_case(lr, a, b, f"local tile {tile} {(rows, L, D)} chunks={plan['chunks']}")
