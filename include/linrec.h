@@ -59,12 +59,15 @@ typedef enum linrec_status {
  * device memory of the current HIP device, each inside one allocation of at
  * least B*L*D*4 bytes (checked with the HIP runtime before launch).
  *
- * Workspace: when L spans several tiles the call uses a per-device workspace
- * that the library allocates on first need (hipMalloc, outside any stream),
- * grows when a larger shape needs more, and frees in linrec_release().  Calls
- * on one device share it, so calls that may overlap in time on one device
- * must be ordered on one stream; calls on different streams of one device
- * race.  Buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
+ * Workspace: when L spans several tiles and the tiles must look back across
+ * workgroups, the call uses a per-device workspace that the library
+ * allocates on first need (hipMalloc, outside any stream), grows when a
+ * larger shape needs more, and frees in linrec_release().  Calls on one
+ * device share it, so calls that may overlap in time on one device must be
+ * ordered on one stream; calls on different streams of one device race.
+ * When the persistent workgroups can take whole (batch row, channel slab)
+ * sequences, 1 to 4 each, the carry stays inside each workgroup and the call
+ * touches no workspace.  Buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
  * aligned buffers with D % 4 == 0 use 128-bit accesses, anything else the
  * 32-bit form of the same kernel.
  *
@@ -74,10 +77,12 @@ typedef enum linrec_status {
  * synchronisation.
  *
  * Environment: LINREC_TILE="t=<steps per lane>,w=<data waves per workgroup>,
- * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>" overrides the
- * tile shape, the kernel (m=0: persistent workgroups that take tiles in turn;
- * m=1: one workgroup per tile) and the launch size the library picks (each key
- * optional; unsupported values are rejected with LINREC_ERR_INVALID_ARGUMENT).
+ * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>,l=<0|1>"
+ * overrides the tile shape, the kernel (m=0: persistent workgroups that take
+ * tiles in turn; m=1: one workgroup per tile), whether persistent workgroups
+ * may keep the carry local (l=1, the default; l=0 makes every tile look back)
+ * and the launch size the library picks (each key optional; unsupported values
+ * are rejected with LINREC_ERR_INVALID_ARGUMENT).
  * LINREC_SPIN_LIMIT=<n> overrides how many times a tile polls a predecessor's
  * status before it recomputes that predecessor's pair from a and b itself
  * (see linrec_device_timeouts); results are the same either way, so it exists
@@ -99,15 +104,16 @@ typedef struct linrec_plan {
     int64_t chunks;          /* tiles along L for one (batch row, channel slab)        */
     int64_t tiles;           /* tiles of the problem (0 if empty); mode 1 launches one
                                 workgroup per tile, mode 0 at most as many as fit     */
-    size_t workspace_bytes;  /* device workspace needed (0 when chunks <= 1)           */
+    size_t workspace_bytes;  /* device workspace the tiles need if they look back (0
+                                when chunks <= 1); unused when the carry stays local  */
     int32_t mode;            /* 0: persistent workgroups take tiles in turn;
                                 1: one workgroup per tile                              */
 } linrec_plan;
 
 /*
  * linrec_scan_plan -- fills *plan for a linrec_scan of shape (B, L, D) whose
- * buffers are 16-byte aligned (aligned16 != 0) or not.  Pure host arithmetic,
- * no HIP call.  Returns LINREC_ERR_INVALID_ARGUMENT for negative or
+ * buffers are 16-byte aligned (aligned16 != 0) or not, on a 256-CU MI355X.
+ * Pure host arithmetic, no HIP call.  Returns LINREC_ERR_INVALID_ARGUMENT for negative or
  * overflowing sizes, an unsupported LINREC_TILE or a null plan.
  */
 linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan *plan);
