@@ -79,6 +79,10 @@ def parse_args():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=li.HEADLINE, choices=sorted(li.WORKLOADS))
+    p.add_argument("--dtype", default="f32", choices=["f32", "bf16", "f16"],
+                   help="storage type of a, b and h (arithmetic is fp32); not f32 runs linrec_scan_ex")
+    p.add_argument("--reverse", action="store_true", help="the reverse-time recurrence (linrec_scan_ex)")
+    p.add_argument("--state", action="store_true", help="pass an initial state and ask for the final state")
     p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -140,15 +144,16 @@ def traffic_from(fetch_csv, write_csv, workload):
     print(json.dumps(rec))
 
 
-def cpu_baseline(a_np, b_np, h_last, seconds: float, shape):
+def cpu_baseline(a_np, b_np, h_last, seconds: float, shape, reverse=False, h_init=None):
     import oracle
 
     threads = oracle.default_threads()
+    fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
     n = a_np.size
     passes, ref = 0, None
     t0 = time.perf_counter()
     while True:
-        ref = oracle.linrec_oracle_f64(a_np, b_np, threads=threads)
+        ref = fn(a_np, b_np, h_init=h_init, threads=threads)
         passes += 1
         elapsed = time.perf_counter() - t0
         if elapsed >= seconds:
@@ -190,19 +195,36 @@ def main():
     seed = w.seeds[0]
     a_np, b_np = li.workload_inputs(args.workload, seed)
     n = a_np.size
-    step_bytes = 12 * n
+    storage = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.dtype]
+    elem = 4 if args.dtype == "f32" else 2
+    plain = args.dtype == "f32" and not args.reverse and not args.state
+    # algorithmic bytes: read a and b, write h, plus the initial and final states
+    step_bytes = 3 * elem * n + (8 * w.B * w.D if args.state else 0)
     sets = args.sets if args.sets > 0 else max(1, math.ceil(1.0e9 / step_bytes))
-    # each set is uploaded from host memory (no device-side copy kernels, so the
-    # calibration copies are the only copy dispatches in a counter profile)
-    a_sets = [torch.from_numpy(a_np).cuda() for _ in range(sets)]
-    b_sets = [torch.from_numpy(b_np).cuda() for _ in range(sets)]
+    # each set is uploaded from host memory (converted to the storage type on
+    # the host: no device-side copy kernels, so the calibration copies are the
+    # only copy dispatches in a counter profile)
+    a_host = torch.from_numpy(a_np).to(storage)
+    b_host = torch.from_numpy(b_np).to(storage)
+    a_sets = [a_host.cuda() for _ in range(sets)]
+    b_sets = [b_host.cuda() for _ in range(sets)]
     h_sets = [torch.empty_like(a_sets[0]) for _ in range(sets)]
+    h0_np = np.random.default_rng(seed + 1000).standard_normal((w.B, w.D)).astype(np.float32) if args.state else None
+    h0 = torch.from_numpy(h0_np).cuda() if args.state else None
+    hf = torch.empty((w.B, w.D), dtype=torch.float32, device="cuda") if args.state else None
     stream = torch.cuda.current_stream()
-    plan = lr.linrec_scan_plan(w.B, w.L, w.D)
+    plan = (lr.linrec_scan_plan(w.B, w.L, w.D) if plain else
+            lr.plan_for(a_sets[0], b_sets[0], h_sets[0], h_init=h0, h_final=hf, reverse=args.reverse))
+
+    def step(k):
+        if plain:
+            lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
+        else:
+            lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream, h_init=h0, h_final=hf,
+                           reverse=args.reverse)
 
     for i in range(args.warmup):
-        k = i % sets
-        lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
+        step(i % sets)
     torch.cuda.synchronize()
 
     # one event pair on the launch stream brackets the timed launches, which run
@@ -212,8 +234,7 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        k = (args.warmup + i) % sets
-        lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
+        step((args.warmup + i) % sets)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -224,8 +245,12 @@ def main():
     value = step_bytes / (wall / args.steps) / 1e9
     achieved = step_bytes / (launch_us * 1e-6) / 1e9
 
+    variant = "" if plain else " (linrec_scan_ex: " + ", ".join(
+        x for x in (f"{args.dtype} storage" if args.dtype != "f32" else "", "reverse time" if args.reverse else "",
+                    "initial and final state" if args.state else "") if x) + ")"
+    headline = args.workload == li.HEADLINE and plain
     out = {
-        "metric": METRIC if args.workload == li.HEADLINE else f"achieved HBM GB/s, linrec_scan {w.describe()}",
+        "metric": METRIC if headline else f"achieved HBM GB/s, linrec_scan {w.describe()}{variant}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -238,8 +263,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {w.describe()}",
+            "workload": f"{args.workload}: {w.describe()}{variant}",
             "B": w.B, "L": w.L, "D": w.D, "seed": seed,
+            "storage": args.dtype, "reverse": args.reverse, "state": args.state,
+            "algorithmic_bytes_per_step": step_bytes,
             "buffer_sets": sets,
             "plan": plan,
         },
@@ -252,7 +279,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload) if plain else None,
         },
         "cpu_baseline": None,
     }
@@ -264,8 +291,10 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
-        h_last = h_sets[last].cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(a_np, b_np, h_last, args.cpu_seconds, (w.B, w.L, w.D))
+        # the oracle on the values the GPU consumed (16-bit inputs widen exactly)
+        h_last = h_sets[last].float().cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(a_host.float().numpy(), b_host.float().numpy(), h_last, args.cpu_seconds,
+                                           (w.B, w.L, w.D), reverse=args.reverse, h_init=h0_np)
     print(json.dumps(out), flush=True)
 
 

@@ -78,11 +78,32 @@ int64_t lanes_for(int p, int64_t quads) {
 //    fewer than 32 sequences each chain is long, and one workgroup per tile,
 //    15 data waves and a single carry wave (64-channel slabs) keep more tiles
 //    in flight along each chain.
-TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus) {
+//  With 16-bit storage and 4 channels per lane, a lane's loads are 8 bytes,
+//  so narrow slabs give short row segments and the pipeline does not shorten
+//  with the bytes; these plans stream more per tile instead (B=32 L=4096
+//  D=256 bf16: 50.6 us against 80.1 us with the fp32 plan; B=8 L=16384
+//  D=1024: 172 against 301 us; B=16 L=512 D=8192: 72.6 us; B=2 L=262144
+//  D=64: 63.5 us): 8 positions per lane and 8 data waves, a local carry over
+//  64- or 32-lane slabs when possible, else 32-lane slabs looking back; with
+//  few sequences, one workgroup per tile of 15 data waves of 4 positions over
+//  16-lane slabs.
+TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int es) {
     const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
     if (n <= 65536.0) return TileShape{vec, 4, 1, 64, 0, 0, 1};
     const int64_t quads = (D + vec - 1) / vec;
+    if (es == 2 && vec == 4) {
+        auto seqs = [&](int p) { return B * ((quads + lanes_for(p, quads) - 1) / lanes_for(p, quads)); };
+        auto local = [&](int p) {
+            for (int m = 1; m <= linrec::kMaxLocalSeqs; ++m)
+                if (seqs(p) % m == 0 && seqs(p) / m >= cus) return true;
+            return false;
+        };
+        for (int p = 64; p >= 32; p >>= 1)
+            if (local(p)) return TileShape{vec, 8, 8, p, 0, 0, 1};
+        if (seqs(32) >= 32) return TileShape{vec, 8, 8, 32, 0, 0, 1};
+        return TileShape{vec, 4, 15, 16, 0, 1, 1};
+    }
     for (int p = 32; p >= 8; p >>= 1) {
         const int64_t lanes = lanes_for(p, quads);
         const int64_t nseq = B * ((quads + lanes - 1) / lanes);
@@ -259,7 +280,7 @@ struct Plan {
 
 linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     const linrec_scan_desc& q = pr.desc;
-    TileShape s = default_tile(q.B, q.L, q.D, pr.vec4, cus);
+    TileShape s = default_tile(q.B, q.L, q.D, pr.vec4, cus, pr.es);
     if (!tile_supported(s)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
     std::string err;
     if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
