@@ -22,15 +22,18 @@
 //   workgroup either persistent (scan_tiles: W data waves and ceil(SC/64)
 //            carry waves take tiles blockIdx, blockIdx + grid, ... in order,
 //            the next tile's loads in flight while the current one waits for
-//            its carry) or one per tile (scan_one).
+//            its carry) or one per tile (scan_one, which always looks back).
 //   steps    (1) load a, b for the lane's T positions;
 //            (2) per-lane sequential composition -> the lane's pair;
 //            (3) exclusive scan of the G group pairs across the wave;
 //            (4) wave pairs -> LDS -> per channel, the tile pair;
-//            (5) cross-workgroup carry by decoupled lookback in the carry wave,
-//                one channel per lane: publish the tile pair, read the status
-//                of the next K predecessors in one round trip, fold their pairs
-//                until one has published its inclusive state, publish ours;
+//            (5) the state entering the tile, in the carry wave, one channel
+//                per lane: kept in LDS when the workgroup's previous tile was
+//                the sequence's previous chunk (a persistent grid that divides
+//                the sequences: local carry), else by decoupled lookback:
+//                publish the tile pair, read the status of the next K
+//                predecessors in one round trip, fold their pairs until one
+//                has published its inclusive state, publish ours;
 //            (6) the carry wave turns the wave pairs into the state entering
 //                each wave; replay h = fma(a, h, b) from it, store.
 //
