@@ -67,7 +67,16 @@ typedef enum linrec_status {
  * ordered on one stream; calls on different streams of one device race.
  * When the persistent workgroups can take whole (batch row, channel slab)
  * sequences, 1 to 4 each, the carry stays inside each workgroup and the call
- * touches no workspace.  Buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
+ * touches no workspace.
+ *
+ * Graph capture: a call enqueues kernel launches only (no memset, no copy), so
+ * it can be captured into a HIP graph and replayed, provided the workspace it
+ * needs already exists -- make one call of the same or a larger shape on the
+ * device before capturing, since allocating is not allowed while capturing.
+ * Replays need no host work between them: each call's lookback epoch advances
+ * inside the kernel.
+ *
+ * Alignment: buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
  * aligned buffers with D % 4 == 0 use 128-bit accesses, anything else the
  * 32-bit form of the same kernel.
  *

@@ -324,3 +324,38 @@ def test_every_local_tile_shape(lr, tile_env, tile):
         plan = lr.linrec_scan_plan(rows, L, D)
         assert plan["lanes_per_row"] == 8 and plan["vec"] == vec
         check_case(lr, a, b, f"local tile {tile} {(rows, L, D)} chunks={plan['chunks']}")
+
+
+@pytest.mark.parametrize("shape", [(32, 4096, 256), (4, 3000, 256), (2, 20000, 64)],
+                         ids=["local_carry", "lookback_persistent", "lookback_one_tile"])
+def test_graph_capture_and_replay(lr, shape):
+    """linrec_scan captured into a HIP graph (after a first call has sized the workspace) and
+    replayed with new inputs each time, with eager work and synchronisation between replays;
+    every replay must match the oracle.  The call records only kernel launches (no memset, no
+    allocation), and a lookback's call epoch advances inside the kernel, so replays stay valid."""
+    B, L, D = shape
+    a = torch.empty(shape, device="cuda")
+    b = torch.empty(shape, device="cuda")
+    h = torch.empty(shape, device="cuda")
+    a0, b0 = li.make_inputs(B, L, D, seed=1700, a_lo=0.5, a_hi=1.0)
+    a.copy_(torch.from_numpy(a0))
+    b.copy_(torch.from_numpy(b0))
+    lr.linrec_scan(a, b, h)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lr.linrec_scan(a, b, h)
+    for k in range(3):
+        a_np, b_np = li.make_inputs(B, L, D, seed=1701 + k, a_lo=0.5, a_hi=1.0)
+        a.copy_(torch.from_numpy(a_np))
+        b.copy_(torch.from_numpy(b_np))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        worst, where = error_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
+        say(f"[graph] {shape} replay {k}: max ratio {worst:.3e}")
+        assert worst <= TOL, (k, worst, where)
+        # eager use of the library between replays
+        h_eager = lr.linrec_scan(a, b)
+        torch.cuda.synchronize()
+        assert error_ratio(h_eager, oracle.linrec_oracle_f64(a_np, b_np))[0] <= TOL
