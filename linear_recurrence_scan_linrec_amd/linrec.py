@@ -142,17 +142,23 @@ def _operand(t) -> linrec_operand:
     return linrec_operand(t.data_ptr(), t.stride(0), t.stride(1))
 
 
-def _check_operand(name, t, shape=None, dtype=None, device=None):
+def _check_operand(name, t, like=None):
+    """Checks one (B, L, D) operand; with `like` (a's size, dtype and device index), that it
+    matches.  Returns the operand's (size, dtype, device index)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda or t.dim() != 3:
+    size = t.size()
+    if not t.is_cuda or len(size) != 3:
         raise ValueError(f"{name} must be a CUDA tensor of shape (B, L, D)")
-    if t.dtype not in DTYPES:
-        raise ValueError(f"{name} must be float32, bfloat16 or float16, not {t.dtype}")
-    if t.shape[2] > 1 and t.stride(2) != 1:
+    dtype = t.dtype
+    if dtype not in DTYPES:
+        raise ValueError(f"{name} must be float32, bfloat16 or float16, not {dtype}")
+    if size[2] > 1 and t.stride()[2] != 1:
         raise ValueError(f"{name} must have unit stride along D (the last dimension)")
-    if shape is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device):
-        raise ValueError(f"{name} must be shaped, typed and placed like a: {tuple(shape)} {dtype} {device}")
+    sig = (size, dtype, t.get_device())
+    if like is not None and sig != like:
+        raise ValueError(f"{name} must be shaped, typed and placed like a: {tuple(like[0])} {like[1]} cuda:{like[2]}")
+    return sig
 
 
 def _check_state(name, t, B, D, device):
@@ -171,6 +177,27 @@ def make_desc(a, b, h, h_init=None, h_final=None, reverse=False) -> linrec_scan_
                             None if h_final is None else h_final.data_ptr())
 
 
+# torch's raw current-stream query (one C call); the public form builds a Stream object first.
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_ptr(stream, index: int) -> int:
+    if stream is not None:
+        return stream.cuda_stream
+    if _current_raw_stream is not None:
+        return _current_raw_stream(index)
+    return torch.cuda.current_stream(index).cuda_stream
+
+
+def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr):
+    if plain:
+        B, L, D = a.size()
+        _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, stream_ptr))
+    else:
+        desc = make_desc(a, b, h, h_init, h_final, reverse)
+        _check(_lib.linrec_scan_ex(ctypes.byref(desc), stream_ptr))
+
+
 def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_final=False, reverse=False):
     """The channel-wise linear recurrence on the GPU.
 
@@ -187,33 +214,28 @@ def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_
     Returns ``h``, or ``(h, h_final)`` when a final state is asked for.  The call is enqueued on
     ``stream`` (default: the current stream of a's device) and returns without synchronising.
     """
-    _check_operand("a", a)
-    _check_operand("b", b, a.shape, a.dtype, a.device)
-    B, L, D = a.shape
+    like = _check_operand("a", a)
+    _check_operand("b", b, like)
+    (B, L, D), dtype, index = like
     if h is None:
-        h = torch.empty((B, L, D), dtype=a.dtype, device=a.device)
+        h = torch.empty((B, L, D), dtype=dtype, device=a.device)
     else:
-        _check_operand("h", h, a.shape, a.dtype, a.device)
-    _check_state("h_init", h_init, B, D, a.device)
+        _check_operand("h", h, like)
     want_final = return_final or h_final is not None
-    if want_final and h_final is None:
-        h_final = torch.empty((B, D), dtype=torch.float32, device=a.device)
-    _check_state("h_final", h_final, B, D, a.device)
-    plain = (a.dtype == torch.float32 and not reverse and h_init is None and h_final is None
-             and a.is_contiguous() and b.is_contiguous() and h.is_contiguous())
-
-    def call(s):
-        if plain:
-            _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, s.cuda_stream))
+    if h_init is not None:
+        _check_state("h_init", h_init, B, D, a.device)
+    if want_final:
+        if h_final is None:
+            h_final = torch.empty((B, D), dtype=torch.float32, device=a.device)
         else:
-            desc = make_desc(a, b, h, h_init, h_final, reverse)
-            _check(_lib.linrec_scan_ex(ctypes.byref(desc), s.cuda_stream))
-
-    if a.device.index == torch.cuda.current_device():
-        call(torch.cuda.current_stream() if stream is None else stream)
+            _check_state("h_final", h_final, B, D, a.device)
+    plain = (dtype is torch.float32 and not reverse and h_init is None and not want_final
+             and a.is_contiguous() and b.is_contiguous() and h.is_contiguous())
+    if index != torch.cuda.current_device():
+        with torch.cuda.device(index):   # the library works on the current HIP device
+            _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index))
     else:
-        with torch.cuda.device(a.device):   # the library works on the current HIP device
-            call(torch.cuda.current_stream(a.device) if stream is None else stream)
+        _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index))
     return (h, h_final) if want_final else h
 
 
