@@ -378,10 +378,10 @@ __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* 
 // their pairs, nearest first, until one of them has published its inclusive
 // state.  A predecessor that shows nothing within spin_limit polls has its pair
 // recomputed from the inputs (`recomputed` is set).  Returns the state that
-// enters the tile; h0 is the state before position 0.
+// enters the tile.
 template <typename S>
 __device__ inline float lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
-                                         int64_t row, int64_t d, float h0, const uint64_t* __restrict__ stat_a,
+                                         int64_t row, int64_t d, const uint64_t* __restrict__ stat_a,
                                          const uint64_t* __restrict__ stat_b, const uint64_t* __restrict__ stat_p,
                                          int64_t idx, int64_t chunk, uint32_t tag_agg, uint32_t tag_inc,
                                          bool& recomputed) {
@@ -437,7 +437,7 @@ __device__ inline float lookback_channel(const S* __restrict__ a, const S* __res
         spins = 0;
     }
     // walked past chunk 0 through recomputed pairs: apply them to the state before position 0
-    return __builtin_fmaf(acc_a, h0, acc_b);
+    return __builtin_fmaf(acc_a, initial_state(g, row, d), acc_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -634,8 +634,10 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
     const float* agg_b = &sh.agg_b[0][0].v[0];
     float h_in = 0.0f;
     if (d < g.D) {
-        const float h0 = initial_state(g, row, d);
-        h_in = h0;
+        // the initial state is read only where it enters: chunk 0 here, or a
+        // lookback that walks back past chunk 0 (a global load on every
+        // tile would put its latency on each hand-over)
+        if (chunk == 0) h_in = initial_state(g, row, d);
         if (g.local_seqs > 0) {
             if (chunk > 0) h_in = *local;
         } else if (g.nchunks > 1) {
@@ -660,7 +662,7 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                     publish(stat_a + idx, tag_agg, ta);
                     publish(stat_b + idx, tag_agg, tb);
                 }
-                h_in = lookback_channel<S>(a, b, g, row, d, h0, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc,
+                h_in = lookback_channel<S>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc,
                                            recomputed);
             }
             if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));

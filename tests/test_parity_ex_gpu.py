@@ -229,6 +229,39 @@ def test_zero_length_passes_the_state(lr):
     assert torch.equal(hf, torch.zeros_like(hf))
 
 
+@pytest.fixture
+def spin_env():
+    old = os.environ.get("LINREC_SPIN_LIMIT")
+    yield
+    if old is None:
+        os.environ.pop("LINREC_SPIN_LIMIT", None)
+    else:
+        os.environ["LINREC_SPIN_LIMIT"] = old
+
+
+@pytest.mark.parametrize("reverse", [False, True], ids=["forward", "reverse"])
+@pytest.mark.parametrize("tile", ["m=0,l=0", "m=1"])
+def test_recompute_with_initial_state(lr, tile, reverse, tile_env, spin_env):
+    """Lookback with the wait for a predecessor forced to zero polls: tiles recompute their
+    predecessors' pairs from a and b, and a walk that passes chunk 0 applies the initial state
+    itself.  Decays near 1 keep h_init visible over several tiles, so a walk that dropped it
+    would fail the bar."""
+    set_tile(tile)
+    B, L, D = 2, 8192, 64
+    a, b, a_np, b_np = device_inputs((B, L, D), 710, a_lo=0.995, a_hi=1.0)
+    h0_np = (10.0 * np.random.default_rng(711).standard_normal((B, D))).astype(np.float32)
+    before = lr.linrec_device_timeouts()
+    os.environ["LINREC_SPIN_LIMIT"] = "0"
+    h, hf = lr.linrec_scan(a, b, h_init=torch.from_numpy(h0_np).cuda(), return_final=True, reverse=reverse)
+    torch.cuda.synchronize()
+    os.environ.pop("LINREC_SPIN_LIMIT")
+    recomputed = lr.linrec_device_timeouts() - before
+    ref = (oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64)(a_np, b_np, h_init=h0_np)
+    label = f"recompute h_init {tile} {'reverse' if reverse else 'forward'} ({recomputed} tiles recomputed)"
+    check(h, ref, torch.float32, label)
+    check(hf, ref[:, 0 if reverse else -1, :], torch.float32, label + " h_final")
+
+
 # ----------------------------------------------------------------------------- reverse time
 
 @pytest.mark.parametrize("tile", TILES)
