@@ -86,12 +86,14 @@ typedef enum linrec_status {
  * synchronisation.
  *
  * Environment: LINREC_TILE="t=<steps per lane>,w=<data waves per workgroup>,
- * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>,l=<0|1>"
+ * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>,l=<0|1>,x=<0|1>"
  * overrides the tile shape, the kernel (m=0: persistent workgroups that take
  * tiles in turn; m=1: one workgroup per tile), whether persistent workgroups
- * may keep the carry local (l=1, the default; l=0 makes every tile look back)
- * and the launch size the library picks (each key optional; unsupported values
- * are rejected with LINREC_ERR_INVALID_ARGUMENT).
+ * may keep the carry local (l=1, the default; l=0 makes every tile look back),
+ * whether channel slabs narrower than a 128-byte line are grouped so that the
+ * slabs sharing a line run on one XCD (x=1, the default; x=0 keeps dispatch
+ * order) and the launch size the library picks (each key optional; unsupported
+ * values are rejected with LINREC_ERR_INVALID_ARGUMENT).
  * LINREC_SPIN_LIMIT=<n> overrides how many times a tile polls a predecessor's
  * status before it recomputes that predecessor's pair from a and b itself
  * (see linrec_device_timeouts); results are the same either way, so it exists

@@ -20,6 +20,8 @@ struct TileShape {
     int m;    // 0: persistent workgroups with carry waves; 1: one tile per workgroup
     int l;    // 1: persistent workgroups keep the carry local when their grid can divide
               // the sequences among them; 0: always look back
+    int x = 1;  // 1: slabs that share a cache line are scanned on one XCD (when rows are
+                // narrower than a line); 0: sequences in dispatch order
 };
 
 // Instantiated tile shapes.  Persistent workgroups keep two register buffers
@@ -34,7 +36,8 @@ inline bool tile_supported(const TileShape& s) {
     const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
     const bool q_ok = s.q >= 0 && s.q <= 64;
     const bool l_ok = s.l == 0 || s.l == 1;
-    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok && l_ok;
+    const bool x_ok = s.x == 0 || s.x == 1;
+    return vec_ok && t_ok && w_ok && m_ok && fits && p_ok && q_ok && l_ok && x_ok;
 }
 
 struct Launch {

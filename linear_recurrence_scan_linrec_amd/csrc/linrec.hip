@@ -124,7 +124,7 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
     return s;
 }
 
-// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0,l=1" (any subset of the keys).
+// LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0,l=1,x=1" (any subset of the keys).
 bool apply_tile_env(TileShape& s, std::string& err) {
     const char* env = std::getenv("LINREC_TILE");
     if (env == nullptr || *env == '\0') return true;
@@ -153,15 +153,16 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         else if (key == "q") s.q = static_cast<int>(val);
         else if (key == "m") s.m = static_cast<int>(val);
         else if (key == "l") s.l = static_cast<int>(val);
+        else if (key == "x") s.x = static_cast<int>(val);
         else {
-            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q, m, l";
+            err = "LINREC_TILE key '" + key + "' is not one of t, w, vec, p, q, m, l, x";
             return false;
         }
         pos = end + 1;
     }
     if (!tile_supported(s)) {
         err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,15}, vec in {1,4}, "
-              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}; not vec=4 with t=16 and m=0, "
+              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}, x in {0,1}; not vec=4 with t=16 and m=0, "
               "not w=15 with vec*t > 16)";
         return false;
     }
@@ -319,6 +320,16 @@ linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
                                                  "plus one carry wave per 64 slab channels); pick a smaller w or p");
     g.nslab = static_cast<int32_t>((quads + lanes - 1) / lanes);
     g.nseq = q.B * g.nslab;
+    // slab rows narrower than a 128-byte line: the slabs of one line go to one
+    // XCD (see sequence_of) when whole lines of slabs fit in each batch row
+    // and the sequences fill whole blocks of 8 lines' slabs
+    g.line_shift = 0;
+    const int64_t row_bytes = static_cast<int64_t>(g.slab_channels) * pr.es;
+    if (s.x == 1 && row_bytes < 128 && 128 % row_bytes == 0) {
+        const int64_t per_line = 128 / row_bytes;
+        if (g.nslab % per_line == 0 && g.nseq % (8 * per_line) == 0)
+            while ((int64_t{1} << g.line_shift) < per_line) ++g.line_shift;
+    }
     g.steps_per_tile = static_cast<int64_t>(s.w) * g.groups * s.t;
     g.nchunks = (q.L + g.steps_per_tile - 1) / g.steps_per_tile;
     int64_t tiles = 0;

@@ -102,6 +102,7 @@ struct Geometry {
     uint32_t spin_limit;   // polls of one predecessor before recomputing its pair
     int32_t reverse;       // 0: position tau is time step tau; 1: time step L-1-tau
     int32_t local_seqs;    // > 0: the persistent grid divides nseq into local_seqs (<= kMaxLocalSeqs)
+    int32_t line_shift;    // log2 of the slabs that share one 128-byte line (0: slots are sequences)
                            // sequences per workgroup, so every tile's predecessor was this
                            // workgroup's own tile local_seqs tiles earlier and the carry stays in
                            // LDS (no status words, no workspace); 0: decoupled lookback
@@ -312,6 +313,21 @@ __device__ __forceinline__ OperandSpot operand_spot(const S* base, int64_t sb, i
     return o;
 }
 
+// Dispatch slot (tile modulo nseq) -> sequence.  A slab row narrower than a
+// 128-byte cache line shares each line with the neighbouring slabs of its
+// batch row: n = 2^line_shift slabs per line.  Within each block of 8n slots,
+// slot x + 8i (x < 8, i < n) takes sequence n*x + i, so the n slabs of one
+// line sit on slots that are equal modulo 8.  Workgroups are dispatched to the
+// 8 XCDs in turn, so those slabs are scanned on one XCD and each line is
+// fetched into one L2 once instead of into n.  The host sets line_shift only
+// when nseq is a multiple of 8n; any value gives a bijection on the slots.
+__device__ __forceinline__ int64_t sequence_of(const Geometry& g, int64_t slot) {
+    if (g.line_shift == 0) return slot;
+    const int64_t block = int64_t{8} << g.line_shift;
+    const int64_t r = slot & (block - 1);
+    return (slot - r) + ((r & 7) << g.line_shift) + (r >> 3);
+}
+
 template <typename S>
 __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const Geometry& g, int64_t tile,
                                            int wave, int quad, int grp, int vec, int T) {
@@ -319,7 +335,7 @@ __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const G
     // the chunk is the slow index: a tile's predecessors come before it in
     // every workgroup's order, and the tiles in flight spread over all sequences
     s.chunk = tile / g.nseq;
-    s.seq = tile - s.chunk * g.nseq;
+    s.seq = sequence_of(g, tile - s.chunk * g.nseq);
     s.row = s.seq / g.nslab;
     s.slab = s.seq - s.row * g.nslab;
     const int64_t d0 = s.slab * g.slab_channels + static_cast<int64_t>(quad) * vec;
@@ -626,7 +642,7 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                                               uint32_t epoch, bool& recomputed, int64_t tile, float* local) {
     if (c >= g.slab_channels) return;
     const int64_t chunk = tile / g.nseq;
-    const int64_t seq = tile - chunk * g.nseq;
+    const int64_t seq = sequence_of(g, tile - chunk * g.nseq);
     const int64_t row = seq / g.nslab;
     const int64_t slab = seq - row * g.nslab;
     const int64_t d = slab * g.slab_channels + c;

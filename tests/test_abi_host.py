@@ -117,7 +117,7 @@ def test_tile_override(tile_env):
         binding.linrec_scan_plan(32, 4096, 256)
     os.environ["LINREC_TILE"] = "w=15,p=16,t=4"
     assert binding.linrec_scan_plan(32, 4096, 256)["waves"] == 15
-    for bad in ("t=5", "w=3", "w=16", "w=5", "vec=2", "t=16", "m=3", "m=2,w=2", "m=2,t=8,w=8", "w=14,t=8", "m=-1", "m=0,vec=4,t=16", "x=1", "t", "t=abc", "p=3", "p=128", "p=0",
+    for bad in ("t=5", "w=3", "w=16", "w=5", "vec=2", "t=16", "m=3", "m=2,w=2", "m=2,t=8,w=8", "w=14,t=8", "m=-1", "m=0,vec=4,t=16", "x=2", "t", "t=abc", "p=3", "p=128", "p=0",
                 "q=-1", "q=65", "d=1"):
         os.environ["LINREC_TILE"] = bad
         with pytest.raises(binding.LinrecError) as err:

@@ -178,6 +178,42 @@ def test_half_storage_named_workloads(lr, dtype):
         del a, b, h
 
 
+# ----------------------------------------------------------------------------- line groups
+
+# tiles whose slab rows are narrower than a 128-byte line, on shapes where whole line groups fill
+# each batch row and the sequences fill whole blocks of 8 groups: the slabs sharing a line are
+# then mapped to slots equal modulo 8 (x=1).  The first four give 256 sequences, one per
+# persistent workgroup on a 256-CU part, so the carry stays local.
+LINE_GROUP_CASES = [
+    (torch.float32, "p=4", (16, 1500, 256)),                 # 64-byte rows, 2 slabs per line
+    (torch.float32, "vec=1,p=8", (8, 1500, 256)),            # 32-byte rows, 4 slabs per line
+    (torch.bfloat16, "p=8", (32, 1500, 256)),                # 64-byte rows
+    (torch.float16, "p=4", (16, 1500, 256)),                 # 32-byte rows
+    (torch.float32, "p=4,l=0", (4, 1500, 256)),              # the same slabs with a lookback
+    (torch.bfloat16, "p=8,m=1,t=4,w=4", (8, 1500, 256)),     # one tile per workgroup
+]
+
+
+@pytest.mark.parametrize("dtype,tile,shape", LINE_GROUP_CASES,
+                         ids=[f"{str(d).split('.')[-1]}-{t}" for d, t, _ in LINE_GROUP_CASES])
+def test_line_groups(lr, dtype, tile, shape, tile_env):
+    """Sequences permuted so that slabs sharing a cache line run on one XCD give the oracle's
+    result; with a local carry the result is bitwise that of dispatch order (x=0), since each
+    sequence is evaluated the same way whichever workgroup runs it."""
+    a, b, a_np, b_np = device_inputs(shape, 750, dtype, a_lo=0.5, a_hi=1.0)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    out = {}
+    for x in (1, 0):
+        set_tile(f"{tile},x={x}")
+        plan = lr.plan_for(a, b)
+        h = lr.linrec_scan(a, b)
+        torch.cuda.synchronize()
+        check(h, ref, dtype, f"line groups {tile} x={x} {tuple(shape)} (lanes {plan['lanes_per_row']})")
+        out[x] = h
+    if "l=0" not in tile and "m=1" not in tile:
+        assert torch.equal(out[1], out[0])
+
+
 # ----------------------------------------------------------------------------- initial / final state
 
 @pytest.mark.parametrize("tile", TILES)
