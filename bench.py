@@ -89,7 +89,7 @@ def parse_args():
                    help="storage type of a, b and h (arithmetic is fp32); not f32 runs linrec_scan_ex")
     p.add_argument("--reverse", action="store_true", help="the reverse-time recurrence (linrec_scan_ex)")
     p.add_argument("--state", action="store_true", help="pass an initial state and ask for the final state")
-    p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB)")
+    p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB, at most warmup + steps)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibration-copy", type=int, default=0, metavar="N",
@@ -206,7 +206,9 @@ def main():
     plain = args.dtype == "f32" and not args.reverse and not args.state
     # algorithmic bytes: read a and b, write h, plus the initial and final states
     step_bytes = 3 * elem * n + (8 * w.B * w.D if args.state else 0)
-    sets = args.sets if args.sets > 0 else max(1, math.ceil(1.0e9 / step_bytes))
+    # enough copies that the rotation spans >= 1 GB (beyond the 256 MB Infinity Cache), but never
+    # more than the run uses: a tiny workload would otherwise allocate ~1e5 copies
+    sets = args.sets if args.sets > 0 else max(1, min(math.ceil(1.0e9 / step_bytes), args.warmup + args.steps))
     # each set is uploaded from host memory (converted to the storage type on
     # the host: no device-side copy kernels, so the calibration copies are the
     # only copy dispatches in a counter profile)
