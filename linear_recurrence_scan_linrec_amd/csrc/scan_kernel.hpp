@@ -328,16 +328,47 @@ __device__ __forceinline__ int64_t sequence_of(const Geometry& g, int64_t slot) 
     return (slot - r) + ((r & 7) << g.line_shift) + (r >> 3);
 }
 
+// Tile index -> (chunk, sequence, batch row, slab).  The operands are
+// wave-uniform, so each division is a scalar instruction sequence on the
+// tile's critical path.  Tiles number fewer than 2^31 (the host refuses more),
+// so the 32-bit form is exact.  Measured on MI355X, same-run A/B: with 16-bit
+// storage, whose tiles move half the bytes, the 32-bit form is 2-10% faster;
+// with fp32 storage the 64-bit form is 3-10% faster on the local-carry plans
+// (the workgroups that share a batch row stay closer in step) and no slower
+// on the others.
+struct TileIndex {
+    int64_t chunk, seq, row, slab;
+};
+
+template <typename S>
+__device__ __forceinline__ TileIndex tile_index(const Geometry& g, int64_t tile) {
+    if constexpr (storage_bytes<S>() == 2) {
+        const uint32_t t = static_cast<uint32_t>(tile);
+        const uint32_t nseq = static_cast<uint32_t>(g.nseq);
+        const uint32_t chunk = t / nseq;
+        const uint32_t seq = static_cast<uint32_t>(sequence_of(g, t - chunk * nseq));
+        const uint32_t nslab = static_cast<uint32_t>(g.nslab);
+        const uint32_t row = seq / nslab;
+        return TileIndex{chunk, seq, row, seq - row * nslab};
+    } else {
+        const int64_t chunk = tile / g.nseq;
+        const int64_t seq = sequence_of(g, tile - chunk * g.nseq);
+        const int64_t row = seq / g.nslab;
+        return TileIndex{chunk, seq, row, seq - row * g.nslab};
+    }
+}
+
 template <typename S>
 __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const Geometry& g, int64_t tile,
                                            int wave, int quad, int grp, int vec, int T) {
     TileSpot s;
     // the chunk is the slow index: a tile's predecessors come before it in
     // every workgroup's order, and the tiles in flight spread over all sequences
-    s.chunk = tile / g.nseq;
-    s.seq = sequence_of(g, tile - s.chunk * g.nseq);
-    s.row = s.seq / g.nslab;
-    s.slab = s.seq - s.row * g.nslab;
+    const TileIndex ix = tile_index<S>(g, tile);
+    s.chunk = ix.chunk;
+    s.seq = ix.seq;
+    s.row = ix.row;
+    s.slab = ix.slab;
     const int64_t d0 = s.slab * g.slab_channels + static_cast<int64_t>(quad) * vec;
     s.d_ok = d0 < g.D;
     const int64_t first = s.chunk * g.steps_per_tile;
@@ -641,10 +672,8 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
                                               uint32_t epoch, bool& recomputed, int64_t tile, float* local) {
     if (c >= g.slab_channels) return;
-    const int64_t chunk = tile / g.nseq;
-    const int64_t seq = sequence_of(g, tile - chunk * g.nseq);
-    const int64_t row = seq / g.nslab;
-    const int64_t slab = seq - row * g.nslab;
+    const TileIndex ix = tile_index<S>(g, tile);
+    const int64_t chunk = ix.chunk, seq = ix.seq, row = ix.row, slab = ix.slab;
     const int64_t d = slab * g.slab_channels + c;
     float* agg_a = &sh.agg_a[0][0].v[0];
     const float* agg_b = &sh.agg_b[0][0].v[0];
