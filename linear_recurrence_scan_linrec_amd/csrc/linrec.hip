@@ -101,8 +101,14 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         };
         for (int p = 64; p >= 32; p >>= 1)
             if (local(p)) return TileShape{vec, 8, 8, p, 0, 0, 1};
-        if (seqs(32) >= 32) return TileShape{vec, 8, 8, 32, 0, 0, 1};
-        return TileShape{vec, 4, 15, 16, 0, 1, 1};
+        // one tile per workgroup (15 waves x 4 steps over 16-lane slabs) while that makes at
+        // most 16 tiles per CU, or when there are too few sequences for persistent lookback;
+        // beyond that its one lookback per workgroup costs more than the persistent plan's
+        const int64_t lanes16 = lanes_for(16, quads);
+        const int64_t steps16 = int64_t{4} * (64 / lanes16) * 15;
+        const int64_t tiles16 = seqs(16) * ((L + steps16 - 1) / steps16);
+        if (tiles16 <= int64_t{16} * cus || seqs(32) < 32) return TileShape{vec, 4, 15, 16, 0, 1, 1};
+        return TileShape{vec, 8, 8, 32, 0, 0, 1};
     }
     for (int p = 32; p >= 8; p >>= 1) {
         const int64_t lanes = lanes_for(p, quads);
