@@ -14,7 +14,9 @@
 //            The state before tau = 0 is zero, or h_init when given (then the
 //            first step uses its a); h_final receives the state after tau = L-1.
 //   tile     (batch row, channel slab, chunk of positions): SC channels x
-//            W*G*T positions.
+//            W*G*T positions.  Tile index = chunk * nseq + slot; the slot maps
+//            to a (batch row, slab) sequence, permuted when slabs narrower than
+//            a cache line would otherwise split their lines across XCDs.
 //   lane     owns VEC consecutive channels (VEC = 4: 128-bit fp32 or 64-bit
 //            16-bit accesses along D) and T consecutive positions, in registers.
 //   wave     64 lanes = G groups of P lanes along tau; the P lanes of a group
@@ -102,10 +104,10 @@ struct Geometry {
     uint32_t spin_limit;   // polls of one predecessor before recomputing its pair
     int32_t reverse;       // 0: position tau is time step tau; 1: time step L-1-tau
     int32_t local_seqs;    // > 0: the persistent grid divides nseq into local_seqs (<= kMaxLocalSeqs)
-    int32_t line_shift;    // log2 of the slabs that share one 128-byte line (0: slots are sequences)
                            // sequences per workgroup, so every tile's predecessor was this
                            // workgroup's own tile local_seqs tiles earlier and the carry stays in
                            // LDS (no status words, no workspace); 0: decoupled lookback
+    int32_t line_shift;    // log2 of the slabs that share one 128-byte line (0: slots are sequences)
 };
 
 template <int VEC> struct Vec { float v[VEC]; };
