@@ -161,8 +161,10 @@ def test_half_storage(lr, dtype, tile, tile_env):
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_half_storage_named_workloads(lr, dtype):
-    """The pages' shape and the near-unit workload with resets, stored in 16 bits."""
-    for name in ("pages_shape", "near_unit_resets"):
+    """The named workloads at full size, stored in 16 bits: one tile per workgroup (the pages'
+    shape, long_sequence), persistent lookback (near_unit_resets, with resets) and a local carry
+    (wide_channels)."""
+    for name in ("pages_shape", "near_unit_resets", "long_sequence", "wide_channels"):
         a_np32, b_np32 = li.workload_inputs(name)
         a = torch.from_numpy(a_np32).cuda().to(dtype)
         b = torch.from_numpy(b_np32).cuda().to(dtype)
