@@ -120,10 +120,9 @@ def counters_by_kernel(path, counter):
     return out
 
 
-def traffic_from(fetch_csv, write_csv, workload):
-    """Scale the counters by what they read for a copy of known size; store and print the result."""
-    fetch = counters_by_kernel(fetch_csv, "FETCH_SIZE")
-    write = counters_by_kernel(write_csv, "WRITE_SIZE")
+def traffic_record(fetch, write, workload):
+    """The traffic record from per-dispatch counter bytes (``counters_by_kernel`` of the FETCH_SIZE
+    and the WRITE_SIZE run): each counter is scaled by what it reads for a copy of known size."""
     for name, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
         if "scan" not in d or "copy" not in d:
             raise SystemExit(f"{name}: need both scan_tiles and copyBuffer dispatches in the csv")
@@ -146,6 +145,13 @@ def traffic_from(fetch_csv, write_csv, workload):
         "scan_dispatches": [len(fetch["scan"]), len(write["scan"])],
         "copy_dispatches": [len(fetch["copy"]), len(write["copy"])],
     }
+    return rec
+
+
+def traffic_from(fetch_csv, write_csv, workload):
+    """Scale the counters by what they read for a copy of known size; store and print the result."""
+    rec = traffic_record(counters_by_kernel(fetch_csv, "FETCH_SIZE"), counters_by_kernel(write_csv, "WRITE_SIZE"),
+                         workload)
     traffic_file(workload).write_text(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec))
 

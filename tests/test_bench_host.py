@@ -1,0 +1,77 @@
+"""Host logic of bench.py (no GPU): the HBM traffic derived from rocprofv3 counter files, and when a
+stored traffic record applies."""
+import csv
+import json
+
+import pytest
+
+import bench
+
+HEADER = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+SCAN = "void linrec::scan_tiles<float, 4, 8, 2>(float const*, float const*, float*, linrec::Geometry, ...)"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def write_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(HEADER)
+        w.writerows(rows)
+    return path
+
+
+def test_counters_by_kernel_keeps_scan_and_copy_rows_in_bytes(tmp_path):
+    path = write_csv(tmp_path / "c.csv", [
+        [1, SCAN, "FETCH_SIZE", 100.0],
+        [2, SCAN, "WRITE_SIZE", 7.0],                   # another counter: ignored
+        [3, COPY, "FETCH_SIZE", 262144.0],
+        [4, "some_other_kernel", "FETCH_SIZE", 5.0],    # another kernel: ignored
+        [5, SCAN, "FETCH_SIZE", 300.0],
+    ])
+    got = bench.counters_by_kernel(path, "FETCH_SIZE")
+    assert got == {"scan": [100.0 * 1024, 300.0 * 1024], "copy": [262144.0 * 1024]}
+
+
+def test_traffic_record_scales_by_the_calibration_copy():
+    # a 512 MiB copy reads as 256 MiB (FETCH_SIZE counts half) and writes as 512 MiB
+    fetch = {"scan": [131072.0 * 1024, 131074.0 * 1024], "copy": [262144.0 * 1024] * 3}
+    write = {"scan": [131072.0 * 1024] * 2, "copy": [524288.0 * 1024] * 3}
+    rec = bench.traffic_record(fetch, write, "pages_shape")
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["read_bytes_per_launch"] == 2 * 131073 * 1024
+    assert rec["written_bytes_per_launch"] == 131072 * 1024
+    assert rec["hbm_bytes_per_launch"] == rec["read_bytes_per_launch"] + rec["written_bytes_per_launch"]
+    assert rec["algorithmic_bytes_per_launch"] == 12 * 32 * 4096 * 256
+    assert rec["scan_dispatches"] == [2, 2] and rec["copy_dispatches"] == [3, 3]
+    assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
+
+
+def test_traffic_record_needs_both_kernels():
+    with pytest.raises(SystemExit):
+        bench.traffic_record({"scan": [1.0]}, {"scan": [1.0], "copy": [1.0]}, "pages_shape")
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
+    src = tmp_path / "k.hpp"
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", [src])
+    src.write_text("int f(int x) { return x + 1; }  // one\n")
+    h1 = bench.kernel_source_hash()
+    src.write_text("/* header */\nint f(int x)   {\n  return x + 1;   // two\n}\n")
+    assert bench.kernel_source_hash() == h1
+    src.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash() != h1
+
+
+def test_measured_traffic_applies_only_to_the_same_kernel_plan_and_workload(tmp_path, monkeypatch):
+    record = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "traffic_file", lambda workload: record)
+    rec = {"workload": "pages_shape", "kernel_source_sha256": bench.kernel_source_hash(),
+           "plan": bench.current_plan("pages_shape"), "hbm_bytes_per_launch": 403000000}
+    record.write_text(json.dumps(rec))
+    assert bench.measured_traffic("pages_shape") == 403000000
+    record.write_text(json.dumps(dict(rec, kernel_source_sha256="0" * 64)))
+    assert bench.measured_traffic("pages_shape") is None
+    record.write_text(json.dumps(dict(rec, plan=dict(rec["plan"], waves=99))))
+    assert bench.measured_traffic("pages_shape") is None
+    record.write_text(json.dumps(rec))
+    assert bench.measured_traffic("wide_channels") is None
