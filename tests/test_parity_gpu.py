@@ -359,3 +359,30 @@ def test_graph_capture_and_replay(lr, shape):
         h_eager = lr.linrec_scan(a, b)
         torch.cuda.synchronize()
         assert error_ratio(h_eager, oracle.linrec_oracle_f64(a_np, b_np))[0] <= TOL
+
+
+@pytest.mark.parametrize("shape", [(2, 1 << 20, 1028), (16, 1 << 17, 1028)], ids=["one_tile", "persistent"])
+def test_more_than_2_31_elements(lr, shape):
+    """B*L*D above 2^31 elements, with batch rows more than 2^32 bytes apart: 64-bit row and
+    status indexing.  Inputs are drawn on the device from a seeded generator (26 GB per case);
+    the oracle checks a few channels, including the last slab's ragged edge, over every step."""
+    B, L, D = shape
+    assert B * L * D > 2 ** 31
+    say(f"[large] {shape}: {B * L * D} elements")
+    gen = torch.Generator(device="cuda").manual_seed(31 + B)
+    a = torch.rand(shape, device="cuda", generator=gen)
+    a.mul_(0.5).add_(0.5)                                   # U(0.5, 1)
+    b = torch.randn(shape, device="cuda", generator=gen)
+    h = lr.linrec_scan(a, b)
+    torch.cuda.synchronize()
+    cols = [0, 5, 511, D - 4, D - 1]
+    a_s = np.ascontiguousarray(a[:, :, cols].cpu().numpy())
+    b_s = np.ascontiguousarray(b[:, :, cols].cpu().numpy())
+    h_s = h[:, :, cols].cpu().numpy()
+    del a, b, h
+    torch.cuda.empty_cache()
+    ref = oracle.linrec_oracle_f64(a_s, b_s)
+    ratio = np.abs(h_s - ref) / (1.0 + np.abs(ref))
+    worst = float(ratio.max())
+    say(f"[large] {shape}: channels {cols}, max ratio {worst:.3e}")
+    assert worst <= TOL, (worst, np.unravel_index(int(np.argmax(ratio)), ratio.shape))
