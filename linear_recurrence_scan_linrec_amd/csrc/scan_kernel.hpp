@@ -58,7 +58,6 @@
 namespace linrec {
 
 constexpr int kWave = 64;
-constexpr int kLookbackWindow = 4;        // predecessors read per round trip
 constexpr uint32_t kKindAggregate = 1u;   // payload: one component of the tile pair
 constexpr uint32_t kKindInclusive = 2u;   // payload: state after the tile's last position
 
@@ -108,6 +107,7 @@ struct Geometry {
                            // workgroup's own tile local_seqs tiles earlier and the carry stays in
                            // LDS (no status words, no workspace); 0: decoupled lookback
     int32_t line_shift;    // log2 of the slabs that share one 128-byte line (0: slots are sequences)
+    int32_t lookback_window;  // predecessors a lookback reads per round trip: 2 or 4
 };
 
 template <int VEC> struct Vec { float v[VEC]; };
@@ -423,12 +423,19 @@ __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* 
 }
 
 // Decoupled lookback for one channel of a tile in chunk `chunk` (> 0): reads
-// the status of up to kLookbackWindow predecessors per round trip and folds
-// their pairs, nearest first, until one of them has published its inclusive
-// state.  A predecessor that shows nothing within spin_limit polls has its pair
+// the status of up to WIN predecessors per round trip and folds their pairs,
+// nearest first, until one of them has published its inclusive state.  A
+// predecessor that shows nothing within spin_limit polls has its pair
 // recomputed from the inputs (`recomputed` is set).  Returns the state that
 // enters the tile.
-template <typename S>
+//
+// The window trades status reads against round trips.  Measured on MI355X
+// (same-run A/B): where the tiles of a chunk-major round look back at each
+// other (persistent workgroups), reading 2 predecessors instead of 4 was
+// 4-15% faster; one tile per workgroup over very long chains (over 64
+// chunks per sequence, most predecessors still pending) is fastest with 4.
+// The host picks WIN through Geometry::lookback_window.
+template <typename S, int WIN>
 __device__ inline float lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                          int64_t row, int64_t d, const uint64_t* __restrict__ stat_a,
                                          const uint64_t* __restrict__ stat_b, const uint64_t* __restrict__ stat_p,
@@ -439,9 +446,9 @@ __device__ inline float lookback_channel(const S* __restrict__ a, const S* __res
     int64_t j = chunk - 1;                    // nearest predecessor not folded yet
     uint32_t spins = 0;
     while (j >= 0) {
-        uint64_t wp[kLookbackWindow], wa[kLookbackWindow], wb[kLookbackWindow];
+        uint64_t wp[WIN], wa[WIN], wb[WIN];
 #pragma unroll
-        for (int m = 0; m < kLookbackWindow; ++m) {
+        for (int m = 0; m < WIN; ++m) {
             wp[m] = wa[m] = wb[m] = 0;
             if (j - m >= 0) {
                 const int64_t k = idx - (chunk - (j - m)) * stride;
@@ -454,7 +461,7 @@ __device__ inline float lookback_channel(const S* __restrict__ a, const S* __res
         bool found = false;
         float h_prev = 0.0f;
 #pragma unroll
-        for (int m = 0; m < kLookbackWindow; ++m) {
+        for (int m = 0; m < WIN; ++m) {
             if (found || folded != m || j - m < 0) continue;   // stopped earlier in this window
             if (tag_of(wp[m]) == tag_inc) {
                 h_prev = payload_of(wp[m]);
@@ -709,8 +716,11 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                     publish(stat_a + idx, tag_agg, ta);
                     publish(stat_b + idx, tag_agg, tb);
                 }
-                h_in = lookback_channel<S>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg, tag_inc,
-                                           recomputed);
+                h_in = g.lookback_window > 2
+                           ? lookback_channel<S, 4>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg,
+                                                    tag_inc, recomputed)
+                           : lookback_channel<S, 2>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg,
+                                                    tag_inc, recomputed);
             }
             if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
         }
