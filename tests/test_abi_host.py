@@ -221,3 +221,26 @@ def test_ex_empty_problems_without_a_final_state_are_noops():
         d = desc(*shape)
         d.a.ptr = d.b.ptr = d.h.ptr = None
         assert lib.linrec_scan_ex(ctypes.byref(d), None) == binding.LINREC_OK
+
+
+# The plans the tile rules pick for the named workloads (on the 256-CU part the plan entry points
+# assume), as measured and chosen: a change to the rules shows up here first.
+DEFAULT_PLANS = {
+    # (B, L, D, dtype): (vec, steps_per_lane, waves, lanes_per_row, mode)
+    (32, 4096, 256, 0): (4, 8, 2, 8, 0),        # fp32 pages shape: local carry over 128-byte rows
+    (16, 512, 8192, 0): (4, 8, 4, 32, 0),       # wide_channels: local carry, 4 sequences per workgroup
+    (8, 16384, 1024, 0): (4, 8, 2, 8, 0),       # near_unit_resets: local carry
+    (2, 262144, 64, 0): (4, 4, 15, 16, 1),      # long_sequence: one tile per workgroup
+    (32, 4096, 256, 1): (4, 4, 15, 16, 1),      # bf16 pages shape: one tile per workgroup (2304 tiles)
+    (16, 512, 8192, 1): (4, 8, 8, 64, 0),       # bf16 wide_channels: local carry over 64-lane slabs
+    (8, 16384, 1024, 1): (4, 8, 8, 32, 0),      # bf16 near_unit_resets: persistent lookback
+    (2, 262144, 64, 1): (4, 4, 15, 16, 1),      # bf16 long_sequence: one tile per workgroup
+}
+
+
+@pytest.mark.parametrize("key", sorted(DEFAULT_PLANS), ids=lambda k: f"{'f32' if k[3] == 0 else 'bf16'}-{k[0]}x{k[1]}x{k[2]}")
+def test_default_plans_of_the_named_workloads(key):
+    B, L, D, dtype = key
+    status, p = ex_plan(desc(B, L, D, dtype=dtype))
+    assert status == binding.LINREC_OK
+    assert (p["vec"], p["steps_per_lane"], p["waves"], p["lanes_per_row"], p["mode"]) == DEFAULT_PLANS[key]
