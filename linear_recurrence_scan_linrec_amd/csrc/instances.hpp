@@ -33,7 +33,9 @@ hipError_t occupancy_one(int* groups_per_cu, int threads) {
 
 template <typename S, int VEC, int T, int W>
 const Launch* launch_entry(int mode) {
-    if constexpr (W == 15 && VEC * T > 16) {
+    // register bytes a lane spends on one buffer of T positions (see tile_supported)
+    constexpr int lane_bytes = VEC * T * (VEC == 4 && linrec::storage_bytes<S>() == 2 ? 2 : 4);
+    if constexpr (W == 15 && lane_bytes > 64) {
         return nullptr;
     } else {
         if (mode == 1) {
@@ -41,7 +43,7 @@ const Launch* launch_entry(int mode) {
                                     &run_one<S, VEC, T, W>, &occupancy_one<S, VEC, T, W>};
             return &one;
         }
-        if constexpr (VEC == 4 && T == 16) {
+        if constexpr (lane_bytes > 128) {
             return nullptr;
         } else {
             static const Launch persistent{reinterpret_cast<const void*>(&linrec::scan_tiles<S, VEC, T, W>),
@@ -75,7 +77,7 @@ const Launch* pick_t(int t, int w, int m) {
 
 template <typename S>
 const Launch* pick_launch(const TileShape& s) {
-    if (!tile_supported(s)) return nullptr;
+    if (!tile_supported(s, linrec::storage_bytes<S>())) return nullptr;
     return s.vec == 4 ? pick_t<S, 4>(s.t, s.w, s.m) : pick_t<S, 1>(s.t, s.w, s.m);
 }
 

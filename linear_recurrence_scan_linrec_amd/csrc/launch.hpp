@@ -24,15 +24,22 @@ struct TileShape {
                 // narrower than a line); 0: sequences in dispatch order
 };
 
-// Instantiated tile shapes.  Persistent workgroups keep two register buffers
-// of T positions x VEC channels, which spill at VEC = 4, T = 16; 15 data waves
-// leave at most 128 registers a lane, which spill when VEC * T > 16.
-inline bool tile_supported(const TileShape& s) {
+// Register bytes a lane spends per channel and position: 4 (fp32 values, or
+// 16-bit values widened on load with VEC = 1), 2 (16-bit values kept packed,
+// VEC = 4).
+inline int register_bytes(int vec, int storage_bytes) { return vec == 4 && storage_bytes == 2 ? 2 : 4; }
+
+// Instantiated tile shapes, for a storage type of storage_bytes per element.
+// Persistent workgroups keep two register buffers of T positions x VEC
+// channels, which spill beyond 128 bytes a lane each; 15 data waves leave at
+// most 128 registers a lane, which spill beyond 64 bytes of positions.
+inline bool tile_supported(const TileShape& s, int storage_bytes = 4) {
     const bool vec_ok = s.vec == 1 || s.vec == 4;
     const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
     const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8 || s.w == 15;
     const bool m_ok = s.m == 0 || s.m == 1;
-    const bool fits = !(s.m == 0 && s.vec == 4 && s.t == 16) && !(s.w == 15 && s.vec * s.t > 16);
+    const int lane_bytes = s.vec * s.t * register_bytes(s.vec, storage_bytes);
+    const bool fits = !(s.m == 0 && lane_bytes > 128) && !(s.w == 15 && lane_bytes > 64);
     const bool p_ok = s.p >= 1 && s.p <= 64 && (s.p & (s.p - 1)) == 0;
     const bool q_ok = s.q >= 0 && s.q <= 64;
     const bool l_ok = s.l == 0 || s.l == 1;

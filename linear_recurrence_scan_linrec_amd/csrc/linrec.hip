@@ -80,13 +80,13 @@ int64_t lanes_for(int p, int64_t quads) {
 //    in flight along each chain.
 //  With 16-bit storage and 4 channels per lane, a lane's loads are 8 bytes,
 //  so narrow slabs give short row segments and the pipeline does not shorten
-//  with the bytes; these plans stream more per tile instead (B=32 L=4096
-//  D=256 bf16: 50.6 us against 80.1 us with the fp32 plan; B=8 L=16384
-//  D=1024: 172 against 301 us; B=16 L=512 D=8192: 72.6 us; B=2 L=262144
-//  D=64: 63.5 us): 8 positions per lane and 8 data waves, a local carry over
-//  64- or 32-lane slabs when possible, else 32-lane slabs looking back; with
-//  few sequences, one workgroup per tile of 15 data waves of 4 positions over
-//  16-lane slabs.
+//  with the bytes; these plans stream more per tile instead: 8 positions per
+//  lane and 8 data waves with a local carry over 64- or 32-lane slabs when
+//  possible; else one workgroup per tile of 15 data waves x 8 positions over
+//  16-lane slabs (the values stay packed in registers, so two such workgroups
+//  fit a CU) while that makes at most 16 tiles per CU; else 32-lane slabs
+//  looking back.  (bf16: B=32 L=4096 D=256 43 us, B=2 L=262144 D=64 48 us,
+//  B=8 L=16384 D=1024 162 us, B=16 L=512 D=8192 72 us.)
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int es) {
     const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
@@ -101,13 +101,14 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         };
         for (int p = 64; p >= 32; p >>= 1)
             if (local(p)) return TileShape{vec, 8, 8, p, 0, 0, 1};
-        // one tile per workgroup (15 waves x 4 steps over 16-lane slabs) while that makes at
-        // most 16 tiles per CU, or when there are too few sequences for persistent lookback;
-        // beyond that its one lookback per workgroup costs more than the persistent plan's
+        // one tile per workgroup (15 waves x 8 steps over 16-lane slabs; the packed 16-bit
+        // registers leave two such workgroups per CU) while that makes at most 16 tiles per
+        // CU, or when there are too few sequences for persistent lookback; beyond that its
+        // one lookback per workgroup costs more than the persistent plan's
         const int64_t lanes16 = lanes_for(16, quads);
-        const int64_t steps16 = int64_t{4} * (64 / lanes16) * 15;
+        const int64_t steps16 = int64_t{8} * (64 / lanes16) * 15;
         const int64_t tiles16 = seqs(16) * ((L + steps16 - 1) / steps16);
-        if (tiles16 <= int64_t{16} * cus || seqs(32) < 32) return TileShape{vec, 4, 15, 16, 0, 1, 1};
+        if (tiles16 <= int64_t{16} * cus || seqs(32) < 32) return TileShape{vec, 8, 15, 16, 0, 1, 1};
         return TileShape{vec, 8, 8, 32, 0, 0, 1};
     }
     for (int p = 32; p >= 8; p >>= 1) {
@@ -131,7 +132,7 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
 }
 
 // LINREC_TILE="t=16,w=4,vec=4,p=64,q=2,m=0,l=1,x=1" (any subset of the keys).
-bool apply_tile_env(TileShape& s, std::string& err) {
+bool apply_tile_env(TileShape& s, int es, std::string& err) {
     const char* env = std::getenv("LINREC_TILE");
     if (env == nullptr || *env == '\0') return true;
     std::string spec(env);
@@ -166,10 +167,11 @@ bool apply_tile_env(TileShape& s, std::string& err) {
         }
         pos = end + 1;
     }
-    if (!tile_supported(s)) {
+    if (!tile_supported(s, es)) {
         err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,15}, vec in {1,4}, "
-              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}, x in {0,1}; not vec=4 with t=16 and m=0, "
-              "not w=15 with vec*t > 16)";
+              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}, x in {0,1}; with r register bytes per "
+              "channel and position (2 for 16-bit storage with vec=4, else 4): vec*t*r <= 128 for m=0 and "
+              "<= 64 for w=15)";
         return false;
     }
     return true;
@@ -288,9 +290,9 @@ struct Plan {
 linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     const linrec_scan_desc& q = pr.desc;
     TileShape s = default_tile(q.B, q.L, q.D, pr.vec4, cus, pr.es);
-    if (!tile_supported(s)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
+    if (!tile_supported(s, pr.es)) return fail(LINREC_ERR_INVALID_ARGUMENT, "internal: default tile not supported");
     std::string err;
-    if (!apply_tile_env(s, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
+    if (!apply_tile_env(s, pr.es, err)) return fail(LINREC_ERR_INVALID_ARGUMENT, err);
     if (s.vec == 4 && !pr.vec4)
         return fail(LINREC_ERR_INVALID_ARGUMENT, "vec=4 needs D % 4 == 0, strides that are multiples of 4 and "
                                                  "operands aligned to 4 elements");

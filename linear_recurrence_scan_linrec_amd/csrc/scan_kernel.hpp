@@ -221,6 +221,62 @@ __device__ __forceinline__ void store_vec(__amdgpu_buffer_rsrc_t r, uint32_t off
     }
 }
 
+// Register form of one position's VEC channels.  fp32 keeps the floats.  With
+// 16-bit storage and VEC = 4 a lane keeps the two loaded 32-bit words (four
+// packed values, half the registers) and widens them where they are used, so
+// it can hold twice the positions in the same registers.
+struct Packed4 {
+    uint32_t w[2];
+};
+template <typename S, int VEC> struct RegOf { using type = Vec<VEC>; };
+template <> struct RegOf<Bf16, 4> { using type = Packed4; };
+template <> struct RegOf<F16, 4> { using type = Packed4; };
+template <typename S, int VEC> using Reg = typename RegOf<S, VEC>::type;
+
+template <typename S, int VEC>
+__device__ __forceinline__ Reg<S, VEC> load_reg(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (storage_bytes<S>() == 2 && VEC == 4) {
+        const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kNontemporal);
+        return Packed4{{t.x, t.y}};
+    } else {
+        return load_vec<S, VEC>(r, off);
+    }
+}
+
+template <typename S, int VEC>
+__device__ __forceinline__ Vec<VEC> widen(const Reg<S, VEC>& x) {
+    if constexpr (storage_bytes<S>() == 2 && VEC == 4) {
+        Vec<VEC> v;
+        v.v[0] = widen_bits(S{}, x.w[0] & 0xffffu); v.v[1] = widen_bits(S{}, x.w[0] >> 16);
+        v.v[2] = widen_bits(S{}, x.w[1] & 0xffffu); v.v[3] = widen_bits(S{}, x.w[1] >> 16);
+        return v;
+    } else {
+        return x;
+    }
+}
+
+// The replay widens the packed words again rather than keep the widened values
+// of the scan alive across the hand-over: an empty asm statement that may
+// "change" the words stops the compiler from reusing the scan's conversions,
+// so only the packed words stay live (no instruction is emitted).
+template <typename S, int VEC>
+__device__ __forceinline__ Reg<S, VEC> rewiden_source(const Reg<S, VEC>& x) {
+    Reg<S, VEC> y = x;
+    if constexpr (storage_bytes<S>() == 2 && VEC == 4) asm volatile("" : "+v"(y.w[0]), "+v"(y.w[1]));
+    return y;
+}
+
+// Every channel of x set to c (0 or 1: exact in every storage type).
+template <typename S, int VEC>
+__device__ __forceinline__ void set_reg(Reg<S, VEC>& x, float c) {
+    if constexpr (storage_bytes<S>() == 2 && VEC == 4) {
+        const uint32_t bits = narrow_bits(S{}, c);
+        x.w[0] = x.w[1] = bits | (bits << 16);
+    } else {
+        x = splat<VEC>(c);
+    }
+}
+
 // Two ways to grow a pair (A, Bv) that stands for a stretch of consecutive steps.
 // then_apply: append the later pair (La, Lb)   -> (La*A, La*Bv + Lb)
 // after:      prepend the earlier pair (Ea, Eb) -> (A*Ea, A*Eb + Bv)
@@ -396,11 +452,11 @@ __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const G
 // All of a is requested before any of b: a lane's requests then walk one
 // array at a time, which measured 2% faster than alternating a and b rows.
 template <typename S, int VEC, int T>
-__device__ __forceinline__ void load_tile(Vec<VEC> (&av)[T], Vec<VEC> (&bv)[T], const TileSpot& s) {
+__device__ __forceinline__ void load_tile(Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T], const TileSpot& s) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) av[j] = load_vec<S, VEC>(s.a.r, s.a.off + j * s.a.step);
+    for (int j = 0; j < T; ++j) av[j] = load_reg<S, VEC>(s.a.r, s.a.off + j * s.a.step);
 #pragma unroll
-    for (int j = 0; j < T; ++j) bv[j] = load_vec<S, VEC>(s.b.r, s.b.off + j * s.b.step);
+    for (int j = 0; j < T; ++j) bv[j] = load_reg<S, VEC>(s.b.r, s.b.off + j * s.b.step);
 }
 
 // The pair of chunk j for one channel, composed directly from a and b: the
@@ -577,11 +633,11 @@ struct LanePrefix {
 // along tau inside the wave, and the wave's pair into LDS.  Without h_init the
 // state before position 0 is zero, so that position's a never contributes: use
 // 0 for it.
-template <int VEC, int T, int W>
+template <typename S, int VEC, int T, int W>
 __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, TileShared<VEC, W>& sh, const TileSpot& s,
-                                                          int lane, int wave, int quad, int grp, Vec<VEC> (&av)[T],
-                                                          Vec<VEC> (&bv)[T]) {
-    if (s.tau0 == 0 && g.h_init == nullptr) av[0] = splat<VEC>(0.0f);
+                                                          int lane, int wave, int quad, int grp,
+                                                          Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T]) {
+    if (s.tau0 == 0 && g.h_init == nullptr) set_reg<S, VEC>(av[0], 0.0f);
     if (g.h_final != nullptr) {
         // positions past L become identity steps (1, 0): they then leave the
         // state of position L-1 unchanged to the end of its lane (no stored
@@ -589,16 +645,16 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
 #pragma unroll
         for (int j = 0; j < T; ++j) {
             if (s.tau0 + j >= g.L) {
-                av[j] = splat<VEC>(1.0f);
-                bv[j] = splat<VEC>(0.0f);
+                set_reg<S, VEC>(av[j], 1.0f);
+                set_reg<S, VEC>(bv[j], 0.0f);
             }
         }
     }
 
     // (2) per-lane sequential composition over the T positions
-    Vec<VEC> la = av[0], lb = bv[0];
+    Vec<VEC> la = widen<S, VEC>(av[0]), lb = widen<S, VEC>(bv[0]);
 #pragma unroll
-    for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, av[j], bv[j]);
+    for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, widen<S, VEC>(av[j]), widen<S, VEC>(bv[j]));
 
     // (3) groups along tau inside the wave: inclusive scan, then shift to exclusive
     LanePrefix<VEC> pre;
@@ -637,15 +693,17 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
 // state there and writes it out.
 template <typename S, int VEC, int T>
 __device__ __forceinline__ void replay_from(const Geometry& g, Vec<VEC> hs, const TileSpot& s, int quad,
-                                            const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
-                                            const Vec<VEC> (&bv)[T]) {
+                                            const LanePrefix<VEC>& pre, const Reg<S, VEC> (&av)[T],
+                                            const Reg<S, VEC> (&bv)[T]) {
     // hs: the state entering this wave's positions
 #pragma unroll
     for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(pre.ex_a.v[i], hs.v[i], pre.ex_b.v[i]);
 #pragma unroll
     for (int j = 0; j < T; ++j) {
+        const Vec<VEC> aj = widen<S, VEC>(rewiden_source<S, VEC>(av[j]));
+        const Vec<VEC> bj = widen<S, VEC>(rewiden_source<S, VEC>(bv[j]));
 #pragma unroll
-        for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(av[j].v[i], hs.v[i], bv[j].v[i]);
+        for (int i = 0; i < VEC; ++i) hs.v[i] = __builtin_fmaf(aj.v[i], hs.v[i], bj.v[i]);
         store_vec<S, VEC>(s.h.r, s.h.off + j * s.h.step, hs);
     }
     // the state after position L-1, written by the lane that holds it: an
@@ -661,8 +719,8 @@ __device__ __forceinline__ void replay_from(const Geometry& g, Vec<VEC> hs, cons
 
 template <typename S, int VEC, int T, int W>
 __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
-                                             int wave, int quad, const LanePrefix<VEC>& pre, const Vec<VEC> (&av)[T],
-                                             const Vec<VEC> (&bv)[T]) {
+                                             int wave, int quad, const LanePrefix<VEC>& pre,
+                                             const Reg<S, VEC> (&av)[T], const Reg<S, VEC> (&bv)[T]) {
     replay_from<S, VEC, T>(g, sh.agg_a[wave][quad], s, quad, pre, av, bv);
 }
 
@@ -749,8 +807,8 @@ struct LocalCarry {
 template <typename S, int VEC, int T, int W>
 __device__ __forceinline__ void data_tile(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
                                           const Geometry& g, TileShared<VEC, W>& sh, int lane, int wave, int quad,
-                                          int grp, int64_t tile, Vec<VEC> (&av)[T], Vec<VEC> (&bv)[T], int64_t next,
-                                          Vec<VEC> (&nav)[T], Vec<VEC> (&nbv)[T]) {
+                                          int grp, int64_t tile, Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T],
+                                          int64_t next, Reg<S, VEC> (&nav)[T], Reg<S, VEC> (&nbv)[T]) {
     // (1) the next tile's loads stay in flight while this tile is scanned,
     // waits for its carry and is stored.  They are issued even when there is
     // no next tile (then every lane's offset is out of range and nothing is
@@ -762,7 +820,7 @@ __device__ __forceinline__ void data_tile(const S* __restrict__ a, const S* __re
         load_tile<S, VEC, T>(nav, nbv, ns);
     }
     const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
-    const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
+    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
     __syncthreads();   // the carry wave has written the states entering the waves
     replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);
@@ -815,7 +873,7 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
     // two register buffers: one tile being scanned, the next one loading.  The
     // first step is peeled so that both ways into the loop start right after
     // the same step, with the same loads and stores in flight.
-    Vec<VEC> a0[T], b0[T], a1[T], b1[T];
+    Reg<S, VEC> a0[T], b0[T], a1[T], b1[T];
     int64_t tile = blockIdx.x;
     if (tile >= g.ntiles) return;
     load_tile<S, VEC, T>(a0, b0, locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T));
@@ -869,9 +927,9 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
     const int quad = lane & (g.lanes_d - 1);
     const int grp = lane >> g.log2_lanes_d;
     const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
-    Vec<VEC> av[T], bv[T];
+    Reg<S, VEC> av[T], bv[T];
     load_tile<S, VEC, T>(av, bv, s);
-    const LanePrefix<VEC> pre = scan_registers<VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
+    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
     __syncthreads();   // the states entering the waves are in LDS
     replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);

@@ -231,10 +231,10 @@ DEFAULT_PLANS = {
     (16, 512, 8192, 0): (4, 8, 4, 32, 0),       # wide_channels: local carry, 4 sequences per workgroup
     (8, 16384, 1024, 0): (4, 8, 2, 8, 0),       # near_unit_resets: local carry
     (2, 262144, 64, 0): (4, 4, 15, 16, 1),      # long_sequence: one tile per workgroup
-    (32, 4096, 256, 1): (4, 4, 15, 16, 1),      # bf16 pages shape: one tile per workgroup (2304 tiles)
+    (32, 4096, 256, 1): (4, 8, 15, 16, 1),      # bf16 pages shape: one tile per workgroup (1152 tiles)
     (16, 512, 8192, 1): (4, 8, 8, 64, 0),       # bf16 wide_channels: local carry over 64-lane slabs
     (8, 16384, 1024, 1): (4, 8, 8, 32, 0),      # bf16 near_unit_resets: persistent lookback
-    (2, 262144, 64, 1): (4, 4, 15, 16, 1),      # bf16 long_sequence: one tile per workgroup
+    (2, 262144, 64, 1): (4, 8, 15, 16, 1),      # bf16 long_sequence: one tile per workgroup
 }
 
 

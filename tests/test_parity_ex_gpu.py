@@ -159,6 +159,36 @@ def test_half_storage(lr, dtype, tile, tile_env):
         check(h, oracle.linrec_oracle_f64(a_np, b_np), dtype, f"{dtype} {tile or 'default'} {shape}")
 
 
+# tiles that exist only because 16-bit values stay packed in registers (4 channels per lane):
+# one tile per workgroup with 15 waves of 8 positions, and persistent tiles of 16 positions
+HALF_TILES = ["m=1,t=8,w=15,p=16", "t=16,w=4,p=32", "t=16,w=2,p=16", "t=16,w=4,p=32,l=0"]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+@pytest.mark.parametrize("tile", HALF_TILES)
+def test_half_storage_packed_tiles(lr, dtype, tile, tile_env):
+    """Packed 16-bit register tiles on ragged shapes: plain, with an initial and a final state
+    (positions past L become identity steps in the packed words), and in reverse time."""
+    set_tile(tile)
+    for k, shape in enumerate(SHAPES):
+        B, L, D = shape
+        a, b, a_np, b_np = device_inputs(shape, 800 + k, dtype, a_lo=0.5, a_hi=1.0)
+        label = f"{dtype} {tile} {shape}"
+        h = lr.linrec_scan(a, b)
+        torch.cuda.synchronize()
+        check(h, oracle.linrec_oracle_f64(a_np, b_np), dtype, label)
+        h0_np = np.random.default_rng(900 + k).standard_normal((B, D)).astype(np.float32)
+        h0 = torch.from_numpy(h0_np).cuda()
+        for reverse in (False, True):
+            h, hf = lr.linrec_scan(a, b, h_init=h0, return_final=True, reverse=reverse)
+            torch.cuda.synchronize()
+            fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
+            ref = fn(a_np, b_np, h_init=h0_np)
+            tag = f"{label} state{' reverse' if reverse else ''}"
+            check(h, ref, dtype, tag)
+            check(hf, ref[:, 0 if reverse else -1, :], torch.float32, tag + " h_final")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_half_storage_named_workloads(lr, dtype):
     """The named workloads at full size, stored in 16 bits: one tile per workgroup (the pages'
