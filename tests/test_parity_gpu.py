@@ -386,3 +386,23 @@ def test_more_than_2_31_elements(lr, shape):
     worst = float(ratio.max())
     say(f"[large] {shape}: channels {cols}, max ratio {worst:.3e}")
     assert worst <= TOL, (worst, np.unravel_index(int(np.argmax(ratio)), ratio.shape))
+
+
+def test_release_then_reallocate_and_grow(lr):
+    """linrec_release frees the per-device workspace (a no-op when there is none).  The next call
+    that looks back allocates and clears a new one, and a larger shape grows it.  Every result
+    meets the bar, and the timeout count reads zero again after a release."""
+    lr.linrec_release()
+    lr.linrec_release()
+    assert lr.linrec_device_timeouts() == 0
+    shapes = ((2, 3000, 64), (2, 3000, 64), (4, 20000, 256))   # the last needs a larger workspace
+    for k, shape in enumerate(shapes):
+        a_np, b_np = li.make_inputs(*shape, seed=1800 + k, a_lo=0.5, a_hi=1.0)
+        h = run_gpu(lr, a_np, b_np)
+        worst, where = error_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
+        say(f"[release] {shape} call {k}: max ratio {worst:.3e}")
+        assert worst <= TOL, (shape, worst, where)
+        if k == 0:
+            lr.linrec_release()
+            assert lr.linrec_device_timeouts() == 0
+    assert lr.linrec_scan_plan(4, 20000, 256)["workspace_bytes"] > lr.linrec_scan_plan(2, 3000, 64)["workspace_bytes"]
