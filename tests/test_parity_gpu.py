@@ -406,3 +406,38 @@ def test_release_then_reallocate_and_grow(lr):
             lr.linrec_release()
             assert lr.linrec_device_timeouts() == 0
     assert lr.linrec_scan_plan(4, 20000, 256)["workspace_bytes"] > lr.linrec_scan_plan(2, 3000, 64)["workspace_bytes"]
+
+
+def test_concurrent_host_threads_on_one_stream(lr):
+    """Four host threads enqueue lookback scans on one stream at once (ctypes releases the GIL, so
+    the library's host code runs concurrently): the workspace bookkeeping is shared under a lock,
+    and the calls, ordered by the stream, all meet the bar."""
+    import threading
+    shape = (2, 6000, 64)
+    cases = []
+    for k in range(4):
+        a_np, b_np = li.make_inputs(*shape, seed=1900 + k, a_lo=0.5, a_hi=1.0)
+        cases.append((a_np, b_np, torch.from_numpy(a_np).cuda(), torch.from_numpy(b_np).cuda(),
+                      torch.empty(shape, device="cuda")))
+    stream = torch.cuda.current_stream()
+    errors = []
+
+    def worker(k):
+        try:
+            _, _, a, b, h = cases[k]
+            for _ in range(10):
+                lr.linrec_scan(a, b, h, stream=stream)
+        except Exception as e:   # reported below: an exception in a thread would be lost
+            errors.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for k, (a_np, b_np, _, _, h) in enumerate(cases):
+        worst, where = error_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
+        say(f"[threads] case {k}: max ratio {worst:.3e}")
+        assert worst <= TOL, (k, worst, where)
