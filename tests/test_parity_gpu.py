@@ -441,3 +441,27 @@ def test_concurrent_host_threads_on_one_stream(lr):
         worst, where = error_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
         say(f"[threads] case {k}: max ratio {worst:.3e}")
         assert worst <= TOL, (k, worst, where)
+
+
+@pytest.mark.parametrize("tile", ["", "l=0", "m=1"], ids=["default", "lookback", "one_tile"])
+def test_non_finite_first_decay_is_ignored(lr, tile, tile_env, spin_env):
+    """a at t = 0 multiplies the zero state before the first step, so it never contributes: an
+    infinite or NaN a_0 leaves every output finite and equal to the oracle's, also when the
+    lookback recomputes predecessors (chunk 0 included) from the inputs."""
+    if tile:
+        os.environ["LINREC_TILE"] = tile
+    B, L, D = 4, 5000, 64
+    a_np, b_np = li.make_inputs(B, L, D, seed=2000, a_lo=0.5, a_hi=1.0)
+    a_np[:, 0, 0::2] = np.float32(np.inf)
+    a_np[:, 0, 1::2] = np.float32(np.nan)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    assert np.isfinite(ref).all()
+    for spin in (None, "0"):
+        if spin is not None:
+            os.environ["LINREC_SPIN_LIMIT"] = spin
+        h = run_gpu(lr, a_np, b_np)
+        os.environ.pop("LINREC_SPIN_LIMIT", None)
+        assert bool(torch.isfinite(h).all())
+        worst, where = error_ratio(h, ref)
+        say(f"[a0] {tile or 'default'} spin={spin}: max ratio {worst:.3e}")
+        assert worst <= TOL, (worst, where)
