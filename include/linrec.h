@@ -224,8 +224,12 @@ const char *linrec_last_error_message(void);
  */
 linrec_status linrec_device_timeouts(uint64_t *count);
 
-/* Frees the per-device workspaces.  The caller must make sure no enqueued
- * linrec_scan is still running on any device. */
+/* Frees the per-device workspaces, synchronising each device that holds one
+ * first.  No other thread may call into the library meanwhile.  A HIP graph
+ * that captured a call whose tiles look back refers to the freed workspace:
+ * do not replay it after linrec_release (capture it again after a first call
+ * has allocated a new workspace).  The next call that needs a workspace
+ * allocates a new one. */
 void linrec_release(void);
 
 #ifdef __cplusplus
