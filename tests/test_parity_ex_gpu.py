@@ -349,6 +349,20 @@ def test_reverse(lr, tile, tile_env):
         check(hf, ref[:, 0, :], torch.float32, f"reverse h_final {tile or 'default'} {shape}")
 
 
+@pytest.mark.parametrize("name", ["pages_shape", "long_sequence"])
+def test_reverse_named_workloads(lr, name):
+    """Reverse time at full size: the local-carry plan of the pages' shape and the long lookback
+    chains of long_sequence, run backwards, with a final state."""
+    a_np, b_np = li.workload_inputs(name)
+    a = torch.from_numpy(a_np).cuda()
+    b = torch.from_numpy(b_np).cuda()
+    h, hf = lr.linrec_scan(a, b, reverse=True, return_final=True)
+    torch.cuda.synchronize()
+    ref = oracle.linrec_oracle_rev_f64(a_np, b_np)
+    check(h, ref, torch.float32, f"reverse {name}")
+    check(hf, ref[:, 0, :], torch.float32, f"reverse {name} h_final")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
 def test_reverse_half_strided(lr, dtype):
     """Reverse time with 16-bit storage and a time-major gradient operand."""
