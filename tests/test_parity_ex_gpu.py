@@ -116,6 +116,22 @@ def test_strided_operands(lr, tile, tile_env):
         assert torch.isnan(h_big[:, :, :pad]).all() and torch.isnan(h_big[:, :, pad + D:]).all()
 
 
+def test_strided_pages_shape(lr):
+    """Strided operands at the pages' full shape: b stored time-major, h written inside a wider
+    padded row (the padding must stay untouched)."""
+    a_np, b_np = li.workload_inputs("pages_shape")
+    B, L, D = a_np.shape
+    a = torch.from_numpy(a_np).cuda()
+    b = torch.from_numpy(np.ascontiguousarray(b_np.transpose(1, 0, 2))).cuda().transpose(0, 1)
+    pad = 4
+    h_big = torch.full((B, L, D + 2 * pad), float("nan"), device="cuda")
+    h = h_big[:, :, pad:pad + D]
+    lr.linrec_scan(a, b, h)
+    torch.cuda.synchronize()
+    check(h, oracle.linrec_oracle_f64(a_np, b_np), torch.float32, "strided pages_shape")
+    assert torch.isnan(h_big[:, :, :pad]).all() and torch.isnan(h_big[:, :, pad + D:]).all()
+
+
 @pytest.mark.parametrize("tile", TILES[:3])
 def test_broadcast_decay(lr, tile, tile_env):
     """One decay row shared by every batch row (batch stride 0) and a decay constant over time
