@@ -230,13 +230,14 @@ def test_half_storage_named_workloads(lr, dtype):
 
 # tiles whose slab rows are narrower than a 128-byte line, on shapes where whole line groups fill
 # each batch row and the sequences fill whole blocks of 8 groups: the slabs sharing a line are
-# then mapped to slots equal modulo 8 (x=1).  The first four give 256 sequences, one per
-# persistent workgroup on a 256-CU part, so the carry stays local.
+# then mapped to slots equal modulo 8 (x=1).  The first five keep the carry local on a 256-CU
+# part: 256 sequences, one per persistent workgroup, or 512, two per workgroup.
 LINE_GROUP_CASES = [
     (torch.float32, "p=4", (16, 1500, 256)),                 # 64-byte rows, 2 slabs per line
     (torch.float32, "vec=1,p=8", (8, 1500, 256)),            # 32-byte rows, 4 slabs per line
     (torch.bfloat16, "p=8", (32, 1500, 256)),                # 64-byte rows
     (torch.float16, "p=4", (16, 1500, 256)),                 # 32-byte rows
+    (torch.float32, "p=4,w=2", (32, 1500, 256)),             # 512 sequences: 2 per workgroup, local
     (torch.float32, "p=4,l=0", (4, 1500, 256)),              # the same slabs with a lookback
     (torch.bfloat16, "p=8,m=1,t=4,w=4", (8, 1500, 256)),     # one tile per workgroup
 ]
