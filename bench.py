@@ -43,7 +43,9 @@ PROFILES = ROOT / "profiles"
 
 
 def traffic_file(workload: str) -> Path:
-    return PROFILES / f"traffic_scan_tiles_{workload}.json"
+    """The counter record of a workload, named for the kernel its plan launches."""
+    kernel = "scan_one" if current_plan(workload)["mode"] == 1 else "scan_tiles"
+    return PROFILES / f"traffic_{kernel}_{workload}.json"
 
 
 def kernel_source_hash() -> str:
@@ -114,7 +116,7 @@ def counters_by_kernel(path, counter):
             if row.get("Counter_Name") != counter:
                 continue
             name = row["Kernel_Name"]
-            key = "scan" if "scan_tiles" in name else ("copy" if "copyBuffer" in name else None)
+            key = "scan" if ("scan_tiles" in name or "scan_one" in name) else ("copy" if "copyBuffer" in name else None)
             if key is not None:
                 out.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)   # KiB -> bytes
     return out
@@ -125,7 +127,7 @@ def traffic_record(fetch, write, workload):
     and the WRITE_SIZE run): each counter is scaled by what it reads for a copy of known size."""
     for name, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
         if "scan" not in d or "copy" not in d:
-            raise SystemExit(f"{name}: need both scan_tiles and copyBuffer dispatches in the csv")
+            raise SystemExit(f"{name}: need both scan kernel and copyBuffer dispatches in the csv")
     f_factor = CALIBRATION_BYTES / float(np.mean(fetch["copy"]))
     w_factor = CALIBRATION_BYTES / float(np.mean(write["copy"]))
     read = float(np.mean(fetch["scan"])) * f_factor

@@ -27,9 +27,15 @@ def test_counters_by_kernel_keeps_scan_and_copy_rows_in_bytes(tmp_path):
         [3, COPY, "FETCH_SIZE", 262144.0],
         [4, "some_other_kernel", "FETCH_SIZE", 5.0],    # another kernel: ignored
         [5, SCAN, "FETCH_SIZE", 300.0],
+        [6, "void linrec::scan_one<float, 4, 4, 15>(float const*, ...)", "FETCH_SIZE", 50.0],
     ])
     got = bench.counters_by_kernel(path, "FETCH_SIZE")
-    assert got == {"scan": [100.0 * 1024, 300.0 * 1024], "copy": [262144.0 * 1024]}
+    assert got == {"scan": [100.0 * 1024, 300.0 * 1024, 50.0 * 1024], "copy": [262144.0 * 1024]}
+
+
+def test_traffic_file_is_named_for_the_planned_kernel():
+    assert bench.traffic_file("pages_shape").name == "traffic_scan_tiles_pages_shape.json"
+    assert bench.traffic_file("long_sequence").name == "traffic_scan_one_long_sequence.json"
 
 
 def test_traffic_record_scales_by_the_calibration_copy():
