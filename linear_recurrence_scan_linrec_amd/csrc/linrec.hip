@@ -83,9 +83,11 @@ int64_t lanes_for(int p, int64_t quads) {
 //  with the bytes; these plans stream more per tile instead: 8 positions per
 //  lane and 8 data waves with a local carry over 64- or 32-lane slabs when
 //  possible; else one workgroup per tile of 15 data waves x 8 positions over
-//  16-lane slabs (the values stay packed in registers, so two such workgroups
-//  fit a CU) while that makes at most 16 tiles per CU; else 32-lane slabs
-//  looking back.  (bf16: B=32 L=4096 D=256 43 us, B=2 L=262144 D=64 48 us,
+//  16-lane slabs (the values stay packed in registers, so 8 positions cost
+//  what 4 cost in fp32) while that makes at most 16 tiles per CU; else 32-lane
+//  slabs looking back.  Measured on gfx950, one such 16-wave workgroup runs on
+//  a CU at a time; tiles of 16 positions per lane were slower (fewer, longer
+//  tiles, each still waiting for its lookback).  (bf16: B=32 L=4096 D=256 43 us, B=2 L=262144 D=64 48 us,
 //  B=8 L=16384 D=1024 162 us, B=16 L=512 D=8192 72 us.)
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int es) {
     const int vec = vec4 ? 4 : 1;
@@ -101,10 +103,10 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         };
         for (int p = 64; p >= 32; p >>= 1)
             if (local(p)) return TileShape{vec, 8, 8, p, 0, 0, 1};
-        // one tile per workgroup (15 waves x 8 steps over 16-lane slabs; the packed 16-bit
-        // registers leave two such workgroups per CU) while that makes at most 16 tiles per
-        // CU, or when there are too few sequences for persistent lookback; beyond that its
-        // one lookback per workgroup costs more than the persistent plan's
+        // one tile per workgroup (15 waves x 8 steps over 16-lane slabs, packed 16-bit
+        // registers) while that makes at most 16 tiles per CU, or when there are too few
+        // sequences for persistent lookback; beyond that its one lookback per workgroup
+        // costs more than the persistent plan's
         const int64_t lanes16 = lanes_for(16, quads);
         const int64_t steps16 = int64_t{8} * (64 / lanes16) * 15;
         const int64_t tiles16 = seqs(16) * ((L + steps16 - 1) / steps16);

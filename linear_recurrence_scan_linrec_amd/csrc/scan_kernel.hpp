@@ -896,9 +896,10 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
 // carry_waves carry waves: the data waves load, scan in registers and hand
 // over through LDS; the carry waves look back for the tile's channels, one
 // per lane; the data waves replay and store.  Keeping the lookback out of the
-// data waves keeps their register count, and so the number of workgroups
-// resident per CU, down; with many resident, the loads of some overlap the
-// lookback of others.
+// data waves keeps their register count down.  While a workgroup looks back
+// its CU has no loads of its own in flight; other CUs load meanwhile (measured
+// on gfx950: one 16-wave workgroup per CU at a time, tiles starting in the
+// order their lookbacks end).
 template <typename S, int VEC, int T, int W>
 __global__ void __launch_bounds__(group_limit(W, VEC))
 scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
