@@ -81,3 +81,11 @@ def test_measured_traffic_applies_only_to_the_same_kernel_plan_and_workload(tmp_
     assert bench.measured_traffic("pages_shape") is None
     record.write_text(json.dumps(rec))
     assert bench.measured_traffic("wide_channels") is None
+
+
+def test_more_than_one_gpu_exits_with_a_message_before_touching_a_device(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err
