@@ -465,3 +465,25 @@ def test_non_finite_first_decay_is_ignored(lr, tile, tile_env, spin_env):
         worst, where = error_ratio(h, ref)
         say(f"[a0] {tile or 'default'} spin={spin}: max ratio {worst:.3e}")
         assert worst <= TOL, (worst, where)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_default_plans_resolve_every_carry_from_status(lr, dtype):
+    """At the four large workloads, the default plans (several of which look back across
+    workgroups) resolve every carry from the status their predecessors publish: the recompute
+    fallback, correct but slow, is never taken.  A persistent grid larger than what the device
+    runs at once, or a tile that waits on one not yet started, would show up here."""
+    for name in ("pages_shape", "long_sequence", "wide_channels", "near_unit_resets"):
+        a_np, b_np = li.workload_inputs(name)
+        a = torch.from_numpy(a_np).cuda().to(dtype)
+        b = torch.from_numpy(b_np).cuda().to(dtype)
+        plan = lr.plan_for(a, b)
+        say(f"[timeouts] {name} {dtype}: mode {plan['mode']}, {plan['tiles']} tiles, {plan['chunks']} chunks")
+        before = lr.linrec_device_timeouts()
+        for _ in range(3):
+            h = lr.linrec_scan(a, b)
+        torch.cuda.synchronize()
+        assert lr.linrec_device_timeouts() == before, name
+        assert torch.isfinite(h.float()).all()
+        del a, b, h
+        torch.cuda.empty_cache()
