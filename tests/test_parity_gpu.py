@@ -472,18 +472,20 @@ def test_default_plans_resolve_every_carry_from_status(lr, dtype):
     """At the four large workloads, the default plans (several of which look back across
     workgroups) resolve every carry from the status their predecessors publish: the recompute
     fallback, correct but slow, is never taken.  A persistent grid larger than what the device
-    runs at once, or a tile that waits on one not yet started, would show up here."""
+    runs at once, or a tile that waits on one not yet started, would show up here.  The count
+    runs from the workspace's allocation (growing it starts a new one), so each workload starts
+    from a released workspace."""
     for name in ("pages_shape", "long_sequence", "wide_channels", "near_unit_resets"):
         a_np, b_np = li.workload_inputs(name)
         a = torch.from_numpy(a_np).cuda().to(dtype)
         b = torch.from_numpy(b_np).cuda().to(dtype)
         plan = lr.plan_for(a, b)
         say(f"[timeouts] {name} {dtype}: mode {plan['mode']}, {plan['tiles']} tiles, {plan['chunks']} chunks")
-        before = lr.linrec_device_timeouts()
+        lr.linrec_release()
         for _ in range(3):
             h = lr.linrec_scan(a, b)
         torch.cuda.synchronize()
-        assert lr.linrec_device_timeouts() == before, name
+        assert lr.linrec_device_timeouts() == 0, name
         assert torch.isfinite(h.float()).all()
         del a, b, h
         torch.cuda.empty_cache()
