@@ -34,3 +34,19 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline(monkeypatc
     assert isinstance(cpu["sample"], str) and cpu["sample"]
     # the oracle's answer for the GPU's last output, within the parity bar
     assert cpu["gpu_check_max_ratio"] <= 1e-4
+
+
+@pytest.mark.parametrize("extra,workload", [(["--workload", "tiny"], "tiny"),
+                                            (["--dtype", "bf16", "--reverse", "--state"], "pages_shape")],
+                         ids=["tiny", "bf16_reverse_state"])
+def test_bench_other_workloads_and_forms(monkeypatch, capsys, extra, workload):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", "--no-cpu-baseline", *extra])
+    print(f"bench.main: {' '.join(extra)}", flush=True)
+    bench.main()
+    lines = [line for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    assert len(lines) == 1
+    r = json.loads(lines[0])
+    assert r["config"]["workload"].startswith(workload) and r["value"] > 0 and r["cpu_baseline"] is None
+    assert r["roofline"]["bound"] == "hbm" and r["roofline"]["achieved"] > 0
+    plain = workload != "pages_shape"   # the second case runs through linrec_scan_ex
+    assert r["roofline"]["traffic"] == (bench.measured_traffic(workload) if plain else None)
