@@ -59,6 +59,7 @@ const Launch* pick_w(int w, int m) {
         case 1: return launch_entry<S, VEC, T, 1>(m);
         case 2: return launch_entry<S, VEC, T, 2>(m);
         case 4: return launch_entry<S, VEC, T, 4>(m);
+        case 7: return launch_entry<S, VEC, T, 7>(m);
         case 8: return launch_entry<S, VEC, T, 8>(m);
         case 15: return launch_entry<S, VEC, T, 15>(m);
         default: return nullptr;

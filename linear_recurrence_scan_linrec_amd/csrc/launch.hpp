@@ -36,7 +36,7 @@ inline int register_bytes(int vec, int storage_bytes) { return vec == 4 && stora
 inline bool tile_supported(const TileShape& s, int storage_bytes = 4) {
     const bool vec_ok = s.vec == 1 || s.vec == 4;
     const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;
-    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 8 || s.w == 15;
+    const bool w_ok = s.w == 1 || s.w == 2 || s.w == 4 || s.w == 7 || s.w == 8 || s.w == 15;
     const bool m_ok = s.m == 0 || s.m == 1;
     const int lane_bytes = s.vec * s.t * register_bytes(s.vec, storage_bytes);
     const bool fits = !(s.m == 0 && lane_bytes > 128) && !(s.w == 15 && lane_bytes > 64);

@@ -75,20 +75,22 @@ int64_t lanes_for(int p, int64_t quads) {
 //    B=16 L=512 D=8192: 32-lane slabs, 134 us against 146 us with 64 lanes.)
 //  - Otherwise the tiles look back: persistent workgroups of 8 data waves, 4
 //    positions per lane and 32 lanes (512 bytes of fp32) per row segment; with
-//    fewer than 32 sequences each chain is long, and one workgroup per tile,
-//    15 data waves and a single carry wave (64-channel slabs) keep more tiles
-//    in flight along each chain.
+//    fewer than 32 sequences each chain is long, and one workgroup per tile
+//    keeps more tiles in flight along each chain: 7 data waves and a carry
+//    wave, 8 positions per lane, 8-lane slabs (B=2 L=262144 D=64: 79 us).
+//    Two such 8-wave workgroups share a CU within the register file (about
+//    100 VGPRs each), so one tile's loads run while another waits for its
+//    carry; 16-wave workgroups of 15 data waves took 102 us once the carry's
+//    products of decays became fp64 (70 VGPRs: one workgroup per CU).
 //  With 16-bit storage and 4 channels per lane, a lane's loads are 8 bytes,
 //  so narrow slabs give short row segments and the pipeline does not shorten
 //  with the bytes; these plans stream more per tile instead: 8 positions per
 //  lane and 8 data waves with a local carry over 64- or 32-lane slabs when
-//  possible; else one workgroup per tile of 15 data waves x 8 positions over
-//  16-lane slabs (the values stay packed in registers, so 8 positions cost
-//  what 4 cost in fp32) while that makes at most 16 tiles per CU; else 32-lane
-//  slabs looking back.  Measured on gfx950, one such 16-wave workgroup runs on
-//  a CU at a time; tiles of 16 positions per lane were slower (fewer, longer
-//  tiles, each still waiting for its lookback).  (bf16: B=32 L=4096 D=256 43 us, B=2 L=262144 D=64 48 us,
-//  B=8 L=16384 D=1024 162 us, B=16 L=512 D=8192 72 us.)
+//  possible; else one workgroup per tile of 7 data waves x 16 positions over
+//  16-lane slabs (the values stay packed in registers, so 16 positions cost
+//  what 8 cost in fp32) while that makes at most 16 tiles per CU; else 32-lane
+//  slabs looking back.  (bf16: B=32 L=4096 D=256 44 us, B=2 L=262144 D=64 51 us,
+//  B=8 L=16384 D=1024 177 us, B=16 L=512 D=8192 73 us.)
 TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int es) {
     const int vec = vec4 ? 4 : 1;
     const double n = static_cast<double>(B) * static_cast<double>(L) * static_cast<double>(D);
@@ -103,14 +105,14 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         };
         for (int p = 64; p >= 32; p >>= 1)
             if (local(p)) return TileShape{vec, 8, 8, p, 0, 0, 1};
-        // one tile per workgroup (15 waves x 8 steps over 16-lane slabs, packed 16-bit
+        // one tile per workgroup (7 waves x 16 steps over 16-lane slabs, packed 16-bit
         // registers) while that makes at most 16 tiles per CU, or when there are too few
         // sequences for persistent lookback; beyond that its one lookback per workgroup
         // costs more than the persistent plan's
         const int64_t lanes16 = lanes_for(16, quads);
-        const int64_t steps16 = int64_t{8} * (64 / lanes16) * 15;
+        const int64_t steps16 = int64_t{16} * (64 / lanes16) * 7;
         const int64_t tiles16 = seqs(16) * ((L + steps16 - 1) / steps16);
-        if (tiles16 <= int64_t{16} * cus || seqs(32) < 32) return TileShape{vec, 8, 15, 16, 0, 1, 1};
+        if (tiles16 <= int64_t{16} * cus || seqs(32) < 32) return TileShape{vec, 16, 7, 16, 0, 1, 1};
         return TileShape{vec, 8, 8, 32, 0, 0, 1};
     }
     for (int p = 32; p >= 8; p >>= 1) {
@@ -127,8 +129,9 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
     const int64_t sequences = B * ((D + vec * lanes - 1) / (vec * lanes));
     if (sequences < 32) {
         s.m = 1;
-        s.w = 15;
-        s.p = 64 / vec;
+        s.t = 8;
+        s.w = 7;
+        s.p = 32 / vec;
     }
     return s;
 }
@@ -170,7 +173,7 @@ bool apply_tile_env(TileShape& s, int es, std::string& err) {
         pos = end + 1;
     }
     if (!tile_supported(s, es)) {
-        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,8,15}, vec in {1,4}, "
+        err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,7,8,15}, vec in {1,4}, "
               "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}, x in {0,1}; with r register bytes per "
               "channel and position (2 for 16-bit storage with vec=4, else 4): vec*t*r <= 128 for m=0 and "
               "<= 64 for w=15)";
@@ -363,7 +366,7 @@ linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     if (g.nchunks > 1) {
         g.nstatus = tiles * g.slab_channels;
         p.workspace_bytes = sizeof(WorkspaceHeader) + linrec::kDoneBytes +
-                            3 * static_cast<size_t>(g.nstatus) * sizeof(uint64_t);
+                            linrec::kStatusArrays * static_cast<size_t>(g.nstatus) * sizeof(uint64_t);
     } else {
         g.nstatus = 0;
         p.workspace_bytes = 0;

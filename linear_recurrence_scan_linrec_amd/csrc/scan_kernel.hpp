@@ -41,10 +41,12 @@
 //
 // Memory: a, b and h each have their own element strides between batch rows
 // and between time steps (the channel stride is 1) and one storage type S
-// (fp32, bf16 or fp16); all arithmetic is fp32.
+// (fp32, bf16 or fp16).  Values are fp32 in registers; outputs are replayed in
+// fp32, and the pairs that carry the state into each lane are fp64 (see
+// "Precision of the carry path" below).
 //
 // Status words are self-validating 64-bit values: the high half is a tag
-// (call epoch << 2 | kind), the low half the fp32 payload, stored and loaded
+// (call epoch << 2 | kind), the low half an fp32 payload, stored and loaded
 // with agent-scope relaxed atomics.  A single 64-bit access is atomic, so no
 // fence orders payload against flag and no per-call clearing is needed: words
 // from earlier calls carry an older epoch.  A predecessor that publishes
@@ -63,11 +65,12 @@ constexpr uint32_t kKindInclusive = 2u;   // payload: state after the tile's las
 
 // Workspace: a header, kDoneSlots slot lines (128 bytes each: word 0 counts
 // the workgroups of the current call that hold the epoch, word 1 is the epoch
-// of the current call), then three status arrays (pair A, pair B, inclusive
-// state) of nstatus words.
+// of the current call), then kStatusArrays status arrays of nstatus words
+// (see StatusArrays).
 constexpr int kMaxLocalSeqs = 4;  // sequences one workgroup may carry locally
 constexpr int kLineWords = 32;    // uint32 words per 128-byte line
 constexpr int kDoneSlots = 256;
+constexpr int kStatusArrays = 4;
 
 struct WorkspaceHeader {
     uint32_t reserved;
@@ -277,36 +280,49 @@ __device__ __forceinline__ void set_reg(Reg<S, VEC>& x, float c) {
     }
 }
 
-// Two ways to grow a pair (A, Bv) that stands for a stretch of consecutive steps.
-// then_apply: append the later pair (La, Lb)   -> (La*A, La*Bv + Lb)
-// after:      prepend the earlier pair (Ea, Eb) -> (A*Ea, A*Eb + Bv)
-template <int VEC>
-__device__ __forceinline__ void then_apply(Vec<VEC>& A, Vec<VEC>& Bv, const Vec<VEC>& La, const Vec<VEC>& Lb) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-        Bv.v[i] = __builtin_fmaf(La.v[i], Bv.v[i], Lb.v[i]);
-        A.v[i] = La.v[i] * A.v[i];
+// Precision of the carry path.  Outputs are replayed in fp32 (h = fma(a, h, b))
+// from the state entering each lane's positions, like a sequential fp32 loop.
+// What carries the state from tile to tile is the product of each stretch's
+// decays, and those products are kept in fp64 from the lane upwards (a lane's
+// product starts from exact products of two fp32 values).  The reason: with a
+// decay that is the same at every step, every lane, wave and tile would round
+// an fp32 product of decays the same way, and the carry multiplies the running
+// state by those products stretch after stretch, so their equal errors would
+// add up along the sequence instead of averaging out (with a decay near 1 and
+// |h| near 100 that exceeds the 1e-4 * (1 + |h|) bar where h crosses zero).
+// The B half of a pair is fp32: its rounding errors follow the b values, so
+// they do not line up.  Values that only seed one lane's or one wave's replay
+// (its prefix pair, the state entering it) are rounded to fp32 once.
+template <int VEC> struct VecD { double v[VEC]; };
+
+// Product of the decays of positions [lo, hi) of a lane, as a tree: the
+// leaves multiply two fp32 values (exact in fp64), the tree is shallow.
+template <int LO, int HI, typename R>
+__device__ __forceinline__ double decay_product(const R& a, int i) {
+    if constexpr (HI - LO == 1) {
+        return static_cast<double>(a[LO].v[i]);
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        return decay_product<LO, MID>(a, i) * decay_product<MID, HI>(a, i);
     }
 }
 
-template <int VEC>
-__device__ __forceinline__ void after(Vec<VEC>& A, Vec<VEC>& Bv, const Vec<VEC>& Ea, const Vec<VEC>& Eb) {
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) {
-        Bv.v[i] = __builtin_fmaf(A.v[i], Eb.v[i], Bv.v[i]);
-        A.v[i] = A.v[i] * Ea.v[i];
-    }
+// Value of `x` held by lane `src` of this wave (ds_bpermute, one per 32-bit half).
+__device__ __forceinline__ double lane_value(double x, int src) {
+    const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(bits)));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(bits >> 32)));
+    return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Value of `x` held by lane `src` of this wave (ds_bpermute).
 __device__ __forceinline__ float lane_value(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-template <int VEC> __device__ __forceinline__ Vec<VEC> lane_value(const Vec<VEC>& x, int src) {
-    Vec<VEC> r;
+template <typename V> __device__ __forceinline__ V lane_values(const V& x, int src) {
+    V r;
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) r.v[i] = lane_value(x.v[i], src);
+    for (int i = 0; i < static_cast<int>(sizeof(x.v) / sizeof(x.v[0])); ++i) r.v[i] = lane_value(x.v[i], src);
     return r;
 }
 
@@ -464,18 +480,30 @@ __device__ __forceinline__ void load_tile(Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv
 // reads inputs, so it always finishes.
 template <typename S>
 __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
-                                              int64_t row, int64_t d, int64_t j, float& A, float& Bv) {
-    A = 1.0f;
-    Bv = 0.0f;
+                                              int64_t row, int64_t d, int64_t j, double& A, double& Bv) {
+    A = 1.0;
+    float bl = 0.0f;
     const int64_t tau_begin = j * g.steps_per_tile;
     const int64_t tau_end = tau_begin + g.steps_per_tile < g.L ? tau_begin + g.steps_per_tile : g.L;
     for (int64_t tau = tau_begin; tau < tau_end; ++tau) {
         const int64_t t = time_of(g, tau);
         const float at = (tau == 0 && g.h_init == nullptr) ? 0.0f : load_one(a + row * g.a_sb + t * g.a_sl + d);
         const float bt = load_one(b + row * g.b_sb + t * g.b_sl + d);
-        Bv = __builtin_fmaf(at, Bv, bt);
-        A = at * A;
+        bl = __builtin_fmaf(at, bl, bt);
+        A = static_cast<double>(at) * A;
     }
+    Bv = bl;
+}
+
+// Status arrays of a lookback workspace, nstatus words each: the tile pair
+// (its product of decays as the fp32 pair hi + lo, which keeps about 48 bits
+// of it, and B), and the inclusive state after the tile.
+struct StatusArrays {
+    uint64_t *a_hi, *a_lo, *b, *p;
+};
+
+__device__ __forceinline__ StatusArrays status_arrays(uint64_t* stat, int64_t nstatus) {
+    return StatusArrays{stat, stat + nstatus, stat + 2 * nstatus, stat + 3 * nstatus};
 }
 
 // Decoupled lookback for one channel of a tile in chunk `chunk` (> 0): reads
@@ -492,43 +520,43 @@ __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* 
 // chunks per sequence, most predecessors still pending) is fastest with 4.
 // The host picks WIN through Geometry::lookback_window.
 template <typename S, int WIN>
-__device__ inline float lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
-                                         int64_t row, int64_t d, const uint64_t* __restrict__ stat_a,
-                                         const uint64_t* __restrict__ stat_b, const uint64_t* __restrict__ stat_p,
-                                         int64_t idx, int64_t chunk, uint32_t tag_agg, uint32_t tag_inc,
-                                         bool& recomputed) {
+__device__ inline double lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
+                                          int64_t row, int64_t d, const StatusArrays& st, int64_t idx, int64_t chunk,
+                                          uint32_t tag_agg, uint32_t tag_inc, bool& recomputed) {
     const int64_t stride = g.slab_channels;   // status distance between consecutive chunks
-    float acc_a = 1.0f, acc_b = 0.0f;
+    double acc_a = 1.0, acc_b = 0.0;
     int64_t j = chunk - 1;                    // nearest predecessor not folded yet
     uint32_t spins = 0;
     while (j >= 0) {
-        uint64_t wp[WIN], wa[WIN], wb[WIN];
+        uint64_t wp[WIN], wh[WIN], wl[WIN], wb[WIN];
 #pragma unroll
         for (int m = 0; m < WIN; ++m) {
-            wp[m] = wa[m] = wb[m] = 0;
+            wp[m] = wh[m] = wl[m] = wb[m] = 0;
             if (j - m >= 0) {
                 const int64_t k = idx - (chunk - (j - m)) * stride;
-                wp[m] = observe(stat_p + k);
-                wa[m] = observe(stat_a + k);
-                wb[m] = observe(stat_b + k);
+                wp[m] = observe(st.p + k);
+                wh[m] = observe(st.a_hi + k);
+                wl[m] = observe(st.a_lo + k);
+                wb[m] = observe(st.b + k);
             }
         }
         int folded = 0;
         bool found = false;
-        float h_prev = 0.0f;
+        double h_prev = 0.0;
 #pragma unroll
         for (int m = 0; m < WIN; ++m) {
             if (found || folded != m || j - m < 0) continue;   // stopped earlier in this window
             if (tag_of(wp[m]) == tag_inc) {
                 h_prev = payload_of(wp[m]);
                 found = true;
-            } else if (tag_of(wa[m]) == tag_agg && tag_of(wb[m]) == tag_agg) {
-                acc_b = __builtin_fmaf(acc_a, payload_of(wb[m]), acc_b);
-                acc_a = acc_a * payload_of(wa[m]);
+            } else if (tag_of(wh[m]) == tag_agg && tag_of(wl[m]) == tag_agg && tag_of(wb[m]) == tag_agg) {
+                const double pa = static_cast<double>(payload_of(wh[m])) + static_cast<double>(payload_of(wl[m]));
+                acc_b = __builtin_fma(acc_a, static_cast<double>(payload_of(wb[m])), acc_b);
+                acc_a = acc_a * pa;
                 folded = m + 1;
             }
         }
-        if (found) return __builtin_fmaf(acc_a, h_prev, acc_b);
+        if (found) return __builtin_fma(acc_a, h_prev, acc_b);
         if (folded > 0) {
             j -= folded;
             spins = 0;
@@ -540,16 +568,16 @@ __device__ inline float lookback_channel(const S* __restrict__ a, const S* __res
             continue;
         }
         // predecessor j shows nothing: compose its pair from the inputs
-        float pa, pb;
+        double pa, pb;
         chunk_pair_from_inputs<S>(a, b, g, row, d, j, pa, pb);
-        acc_b = __builtin_fmaf(acc_a, pb, acc_b);
+        acc_b = __builtin_fma(acc_a, pb, acc_b);
         acc_a = acc_a * pa;
         recomputed = true;
         --j;
         spins = 0;
     }
     // walked past chunk 0 through recomputed pairs: apply them to the state before position 0
-    return __builtin_fmaf(acc_a, initial_state(g, row, d), acc_b);
+    return __builtin_fma(acc_a, static_cast<double>(initial_state(g, row, d)), acc_b);
 }
 
 // ---------------------------------------------------------------------------
@@ -614,13 +642,13 @@ __device__ inline void count_done(WorkspaceHeader* hdr, uint32_t epoch, uint32_t
 }
 
 // LDS shared by the waves of one workgroup.  Between the two barriers of a
-// tile, (agg_a, agg_b)[w] hold data wave w's pair; after the second barrier
-// agg_a[w] holds the state entering wave w's positions (the carry wave
+// tile, (pair_a, pair_b)[w] hold data wave w's pair; after the second barrier
+// pair_b[w] holds the state entering wave w's positions (the carry wave
 // rewrites it in place).  Each data wave reads and writes only its own slot.
 template <int VEC, int W>
 struct TileShared {
-    Vec<VEC> agg_a[W][kWave];   // per data wave and lane channel group
-    Vec<VEC> agg_b[W][kWave];
+    VecD<VEC> pair_a[W][kWave];   // per data wave and lane channel group: the wave's product of decays
+    Vec<VEC> pair_b[W][kWave];    // its B; after the second barrier, the state entering the wave
 };
 
 // What a lane keeps of its tile between the scan in registers and the store.
@@ -652,36 +680,54 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
     }
 
     // (2) per-lane sequential composition over the T positions
-    Vec<VEC> la = widen<S, VEC>(av[0]), lb = widen<S, VEC>(bv[0]);
+    Vec<VEC> in_b = widen<S, VEC>(bv[0]);
 #pragma unroll
-    for (int j = 1; j < T; ++j) then_apply<VEC>(la, lb, widen<S, VEC>(av[j]), widen<S, VEC>(bv[j]));
+    for (int j = 1; j < T; ++j) {
+        const Vec<VEC> aj = widen<S, VEC>(av[j]), bj = widen<S, VEC>(bv[j]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) in_b.v[i] = __builtin_fmaf(aj.v[i], in_b.v[i], bj.v[i]);
+    }
+    VecD<VEC> in_a;
+    {
+        Vec<VEC> aw[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) aw[j] = widen<S, VEC>(av[j]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) in_a.v[i] = decay_product<0, T>(aw, i);
+    }
 
     // (3) groups along tau inside the wave: inclusive scan, then shift to exclusive
     LanePrefix<VEC> pre;
     pre.ex_a = splat<VEC>(1.0f);
     pre.ex_b = splat<VEC>(0.0f);
-    Vec<VEC> wave_a = la, wave_b = lb;
     if (g.groups > 1) {
-        Vec<VEC> in_a = la, in_b = lb;
         for (int off = g.lanes_d; off < kWave; off <<= 1) {
             const int src = (lane - off) & (kWave - 1);
-            const Vec<VEC> pa = lane_value<VEC>(in_a, src);
-            const Vec<VEC> pb = lane_value<VEC>(in_b, src);
-            if (lane >= off) after<VEC>(in_a, in_b, pa, pb);
+            const VecD<VEC> pa = lane_values(in_a, src);
+            const Vec<VEC> pb = lane_values(in_b, src);
+            if (lane >= off) {
+                // prepend the earlier pair (pa, pb)
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) {
+                    in_b.v[i] = __builtin_fmaf(static_cast<float>(in_a.v[i]), pb.v[i], in_b.v[i]);
+                    in_a.v[i] = in_a.v[i] * pa.v[i];
+                }
+            }
         }
         const int prev = (lane - g.lanes_d) & (kWave - 1);
-        const Vec<VEC> pa = lane_value<VEC>(in_a, prev);
-        const Vec<VEC> pb = lane_value<VEC>(in_b, prev);
-        if (grp > 0) { pre.ex_a = pa; pre.ex_b = pb; }
-        const int last = (g.groups - 1) * g.lanes_d + quad;
-        wave_a = lane_value<VEC>(in_a, last);
-        wave_b = lane_value<VEC>(in_b, last);
+        const VecD<VEC> pa = lane_values(in_a, prev);
+        const Vec<VEC> pb = lane_values(in_b, prev);
+        if (grp > 0) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) pre.ex_a.v[i] = static_cast<float>(pa.v[i]);
+            pre.ex_b = pb;
+        }
     }
 
-    // (4) the wave's pair into LDS
-    if (grp == 0) {
-        sh.agg_a[wave][quad] = wave_a;
-        sh.agg_b[wave][quad] = wave_b;
+    // (4) the wave's pair into LDS, from the last group's lanes, which hold it
+    if (grp == g.groups - 1) {
+        sh.pair_a[wave][quad] = in_a;
+        sh.pair_b[wave][quad] = in_b;
     }
     return pre;
 }
@@ -721,7 +767,7 @@ template <typename S, int VEC, int T, int W>
 __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
                                              int wave, int quad, const LanePrefix<VEC>& pre,
                                              const Reg<S, VEC> (&av)[T], const Reg<S, VEC> (&bv)[T]) {
-    replay_from<S, VEC, T>(g, sh.agg_a[wave][quad], s, quad, pre, av, bv);
+    replay_from<S, VEC, T>(g, sh.pair_b[wave][quad], s, quad, pre, av, bv);
 }
 
 // (5) for slab channel c of the tile (one per lane; the caller has passed the
@@ -737,14 +783,14 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
 template <typename S, int VEC, int W>
 __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
-                                              uint32_t epoch, bool& recomputed, int64_t tile, float* local) {
+                                              uint32_t epoch, bool& recomputed, int64_t tile, double* local) {
     if (c >= g.slab_channels) return;
     const TileIndex ix = tile_index<S>(g, tile);
     const int64_t chunk = ix.chunk, seq = ix.seq, row = ix.row, slab = ix.slab;
     const int64_t d = slab * g.slab_channels + c;
-    float* agg_a = &sh.agg_a[0][0].v[0];
-    const float* agg_b = &sh.agg_b[0][0].v[0];
-    float h_in = 0.0f;
+    const double* pair_a = &sh.pair_a[0][0].v[0];
+    float* pair_b = &sh.pair_b[0][0].v[0];
+    double h_in = 0.0;
     if (d < g.D) {
         // the initial state is read only where it enters: chunk 0 here, or a
         // lookback that walks back past chunk 0 (a global load on every
@@ -756,14 +802,12 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
             const bool has_successor = chunk + 1 < g.nchunks;
             const uint32_t tag_agg = (epoch << 2) | kKindAggregate;
             const uint32_t tag_inc = (epoch << 2) | kKindInclusive;
-            uint64_t* stat_a = stat;
-            uint64_t* stat_b = stat + g.nstatus;
-            uint64_t* stat_p = stat + 2 * g.nstatus;
-            float ta = agg_a[c], tb = agg_b[c];
+            const StatusArrays st = status_arrays(stat, g.nstatus);
+            double ta = pair_a[c], tb = pair_b[c];
 #pragma unroll
             for (int v = 1; v < W; ++v) {
-                const float na = agg_a[v * kWave * VEC + c], nb = agg_b[v * kWave * VEC + c];
-                tb = __builtin_fmaf(na, tb, nb);
+                const double na = pair_a[v * kWave * VEC + c], nb = pair_b[v * kWave * VEC + c];
+                tb = __builtin_fma(na, tb, nb);
                 ta = na * ta;
             }
             // status entries are sequence-major: chunk j-1 of a sequence sits
@@ -771,25 +815,25 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
             const int64_t idx = (seq * g.nchunks + chunk) * g.slab_channels + c;
             if (chunk > 0) {
                 if (has_successor) {
-                    publish(stat_a + idx, tag_agg, ta);
-                    publish(stat_b + idx, tag_agg, tb);
+                    const float hi = static_cast<float>(ta);
+                    publish(st.a_hi + idx, tag_agg, hi);
+                    publish(st.a_lo + idx, tag_agg, static_cast<float>(ta - static_cast<double>(hi)));
+                    publish(st.b + idx, tag_agg, static_cast<float>(tb));
                 }
                 h_in = g.lookback_window > 2
-                           ? lookback_channel<S, 4>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg,
-                                                    tag_inc, recomputed)
-                           : lookback_channel<S, 2>(a, b, g, row, d, stat_a, stat_b, stat_p, idx, chunk, tag_agg,
-                                                    tag_inc, recomputed);
+                           ? lookback_channel<S, 4>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed)
+                           : lookback_channel<S, 2>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed);
             }
-            if (has_successor) publish(stat_p + idx, tag_inc, __builtin_fmaf(ta, h_in, tb));
+            if (has_successor) publish(st.p + idx, tag_inc, static_cast<float>(__builtin_fma(ta, h_in, tb)));
         }
     }
-    float hv = h_in;
+    double hv = h_in;
 #pragma unroll
     for (int v = 0; v < W; ++v) {
         const int k = v * kWave * VEC + c;
-        const float na = agg_a[k], nb = agg_b[k];
-        agg_a[k] = hv;
-        hv = __builtin_fmaf(na, hv, nb);
+        const double na = pair_a[k], nb = pair_b[k];
+        pair_b[k] = static_cast<float>(hv);
+        hv = __builtin_fma(na, hv, nb);
     }
     if (g.local_seqs > 0) *local = hv;
 }
@@ -797,7 +841,7 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
 // LDS cells of the local carry: [sequence slot][slab channel].
 template <int VEC>
 struct LocalCarry {
-    float h[kMaxLocalSeqs][kWave * VEC];
+    double h[kMaxLocalSeqs][kWave * VEC];
 };
 
 // Data wave, one tile of the persistent loop: start the loads of the

@@ -84,7 +84,9 @@ def test_plans_for_the_named_workloads():
 
 def test_plan_workspace_covers_status_arrays():
     p = binding.linrec_scan_plan(8, 16384, 1024)
-    per_entry = 3 * 8
+    # four 8-byte status words per (tile, channel): the tile pair's product of decays as an
+    # fp32 hi + lo pair, its B, and the inclusive state
+    per_entry = 4 * 8
     entries = p["tiles"] * p["lanes_per_row"] * p["vec"]
     header, completion_counters = 512, 256 * 128
     assert p["workspace_bytes"] == header + completion_counters + per_entry * entries
@@ -230,11 +232,11 @@ DEFAULT_PLANS = {
     (32, 4096, 256, 0): (4, 8, 2, 8, 0),        # fp32 pages shape: local carry over 128-byte rows
     (16, 512, 8192, 0): (4, 8, 4, 32, 0),       # wide_channels: local carry, 4 sequences per workgroup
     (8, 16384, 1024, 0): (4, 8, 2, 8, 0),       # near_unit_resets: local carry
-    (2, 262144, 64, 0): (4, 4, 15, 16, 1),      # long_sequence: one tile per workgroup
-    (32, 4096, 256, 1): (4, 8, 15, 16, 1),      # bf16 pages shape: one tile per workgroup (1152 tiles)
+    (2, 262144, 64, 0): (4, 8, 7, 8, 1),        # long_sequence: one tile per workgroup, two per CU
+    (32, 4096, 256, 1): (4, 16, 7, 16, 1),      # bf16 pages shape: one tile per workgroup (1280 tiles)
     (16, 512, 8192, 1): (4, 8, 8, 64, 0),       # bf16 wide_channels: local carry over 64-lane slabs
     (8, 16384, 1024, 1): (4, 8, 8, 32, 0),      # bf16 near_unit_resets: persistent lookback
-    (2, 262144, 64, 1): (4, 8, 15, 16, 1),      # bf16 long_sequence: one tile per workgroup
+    (2, 262144, 64, 1): (4, 16, 7, 16, 1),      # bf16 long_sequence: one tile per workgroup
 }
 
 

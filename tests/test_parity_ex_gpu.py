@@ -134,15 +134,8 @@ def test_strided_pages_shape(lr):
 
 @pytest.mark.parametrize("tile", TILES[:3])
 def test_broadcast_decay(lr, tile, tile_env):
-    """One decay row shared by every batch row (batch stride 0) and a decay constant over time
-    (time stride 0).
-
-    The constant decay is kept at or below 0.95: with a decay that is the same at every step,
-    the scan's products of decays round identically in every lane, wave and tile, and those
-    equal rounding errors add up along the carry chain instead of averaging out.  With a decay
-    near 1 and |h| >> 1 that exceeds the 1e-4 bar where h crosses zero (about 1.6x the bar,
-    measured, for decays up to 0.99999 and |h| near 40), while the sequential fp32 loop stays
-    within it."""
+    """One decay row shared by every batch row (batch stride 0), and a decay constant over time
+    (time stride 0) whose per-channel constants run from 0.5 to 0.99999."""
     set_tile(tile)
     B, L, D = 4, 2500, 64
     a_np, b_np = li.make_inputs(1, L, D, seed=301, a_lo=0.9, a_hi=1.0)
@@ -153,12 +146,44 @@ def test_broadcast_decay(lr, tile, tile_env):
     torch.cuda.synchronize()
     check(h, oracle.linrec_oracle_f64(np.broadcast_to(a_np, (B, L, D)), b_np), torch.float32,
           f"batch-broadcast a {tile or 'default'}")
-    c_np, _ = li.make_inputs(1, 1, D, seed=303, a_lo=0.5, a_hi=0.95)
+    # 1 - c log-spaced from 0.5 down to 1e-5 across the channels
+    c_np = (1.0 - np.logspace(np.log10(0.5), -5.0, D)).astype(np.float32).reshape(1, 1, D)
     a_t = torch.from_numpy(c_np).cuda().expand(B, L, D)      # time stride 0
     h = lr.linrec_scan(a_t, b)
     torch.cuda.synchronize()
     check(h, oracle.linrec_oracle_f64(np.broadcast_to(c_np, (B, L, D)), b_np), torch.float32,
           f"time-broadcast a {tile or 'default'}")
+
+
+# the default plan (local carry at this shape), one tile per workgroup (lookback over long
+# chains), the 32-bit form, and persistent workgroups that look back
+CARRY_TILES = ["", "m=1", "vec=1", "t=4,w=8,p=32,l=0"]
+
+
+@pytest.mark.parametrize("decay", [0.999, 0.9999, 0.99999])
+def test_constant_decay_near_one(lr, decay, tile_env):
+    """A decay that is the same at every step and close to 1, at the pages' shape (B=32, L=4096,
+    D=256, b ~ N(0,1), so |h| grows to 80-200 and crosses zero many times), passed both as a
+    time-broadcast operand (time stride 0) and as a materialised tensor, under every carry form.
+
+    Every lane, wave and tile then multiplies the same decays, so a product of decays rounded
+    in fp32 has the same error everywhere and the carry would add those errors up along the
+    sequence; the kernel keeps the products on the carry path in fp64, and the outputs stay
+    within the unchanged bar 1e-4 * (1 + |h|) element by element."""
+    B, L, D = 32, 4096, 256
+    _, b_np = li.make_inputs(B, L, D, seed=310)
+    a_np = np.full((B, L, D), decay, dtype=np.float32)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    say(f"[ex] constant decay {decay}: max |h| = {np.abs(ref).max():.1f}")
+    b = torch.from_numpy(b_np).cuda()
+    a_full = torch.from_numpy(a_np).cuda()
+    a_bcast = torch.full((1, 1, D), decay, dtype=torch.float32, device="cuda").expand(B, L, D)
+    for tile in CARRY_TILES:
+        set_tile(tile)
+        for name, a in (("materialised", a_full), ("time-broadcast", a_bcast)):
+            h = lr.linrec_scan(a, b)
+            torch.cuda.synchronize()
+            check(h, ref, torch.float32, f"constant decay {decay} {name} {tile or 'default'}")
 
 
 # ----------------------------------------------------------------------------- 16-bit storage

@@ -104,7 +104,7 @@ def supported_tiles():
     for m in (0, 1):
         for vec in (1, 4):
             for t in (4, 8, 16):
-                for w in (1, 2, 4, 8, 15):
+                for w in (1, 2, 4, 7, 8, 15):
                     if m == 0 and vec == 4 and t == 16:
                         continue
                     if w == 15 and vec * t > 16:
@@ -306,7 +306,7 @@ def test_local_carry(lr, tile_env, local):
 
 def local_tiles():
     """(vec, t, w) of every persistent instantiation."""
-    return [(vec, t, w) for vec in (1, 4) for t in (4, 8, 16) for w in (1, 2, 4, 8, 15)
+    return [(vec, t, w) for vec in (1, 4) for t in (4, 8, 16) for w in (1, 2, 4, 7, 8, 15)
             if not (vec == 4 and t == 16) and not (w == 15 and vec * t > 16)]
 
 
