@@ -5,14 +5,28 @@ A step is one linrec_scan call over one batch of the chosen workload (default:
 B=32, L=4096, D=256 fp32, a ~ U(0,1), b ~ N(0,1), seeded), inputs already in
 HBM.  Several copies of the inputs and outputs are rotated so that successive
 steps do not find their data in the 256 MB Infinity Cache.  ``value`` is the
-algorithmic HBM throughput, 12 bytes per element (read a, read b, write h),
-over the wall time of exactly --steps steps bracketed by device
-synchronisation.  ``roofline.achieved`` uses the same bytes over the average
-launch duration: HIP events on the launch stream bracket the timed launches,
-which run back to back.
+algorithmic HBM throughput, 12 bytes per element (read a, read b, write h;
+6 with 16-bit storage), over the wall time of exactly --steps steps bracketed
+by device synchronisation.  One HIP event pair on the launch stream brackets
+the timed launches, which run back to back: ``launch_us.mean`` is that span
+over --steps, and ``roofline.achieved`` the algorithmic bytes over it.  (An
+event pair around every launch would add 2-7 us to each measured launch on
+MI355X, measured against rocprofv3's kernel trace, so none is used there.)
 
-The CPU baseline leg times the float64 oracle on the same host arrays for a
-bounded number of seconds and checks the last GPU output against it.
+After the timed region (never inside it):
+* ``launch_us`` median/p10/p90: the means of --regions further regions of 10
+  back-to-back launches, each bracketed the same way.
+* ``ceiling``: the read-two-write-one stream z = x + y of libstream_ceiling.so
+  over the same buffers (the same bytes and rotation), contiguous and in the
+  scan's order over batch rows, each the best of a small sweep of launch
+  shapes timed the same way; ``frac_of_ceiling`` is the scan's achieved rate
+  over the contiguous stream's.
+* ``--cold N``: N single launches, each after a 1 GiB write that evicts the
+  caches, and N single warm launches, each with its own event pair (so both
+  carry the same per-pair overhead and compare with each other).
+* the CPU baseline: the float64 oracle on the same host arrays for a bounded
+  number of seconds, multi-threaded and single-threaded, and a check of the
+  last GPU output against it at the storage type's bar.
 """
 from __future__ import annotations
 
@@ -20,6 +34,7 @@ import argparse
 import hashlib
 import json
 import math
+import os
 import sys
 import time
 from pathlib import Path
@@ -42,10 +57,14 @@ KERNEL_SOURCES = [
 PROFILES = ROOT / "profiles"
 
 
-def traffic_file(workload: str) -> Path:
-    """The counter record of a workload, named for the kernel its plan launches."""
-    kernel = "scan_one" if current_plan(workload)["mode"] == 1 else "scan_tiles"
-    return PROFILES / f"traffic_{kernel}_{workload}.json"
+STORAGE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def traffic_file(workload: str, dtype: str = "f32") -> Path:
+    """The counter record of a workload in a storage type, named for the kernel its plan launches."""
+    kernel = "scan_one" if current_plan(workload, dtype)["mode"] == 1 else "scan_tiles"
+    suffix = "" if dtype == "f32" else f"_{dtype}"
+    return PROFILES / f"traffic_{kernel}_{workload}{suffix}.json"
 
 
 def kernel_source_hash() -> str:
@@ -61,22 +80,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def current_plan(workload: str) -> dict:
+def current_plan(workload: str, dtype: str = "f32") -> dict:
+    """The plan of a forward scan of the workload over contiguous operands of the storage type
+    (host arithmetic only: 16-byte aligned stand-in addresses, nothing is dereferenced)."""
+    import ctypes
+
     from linear_recurrence_scan_linrec_amd import linrec as lr
 
     w = li.WORKLOADS[workload]
-    return lr.linrec_scan_plan(w.B, w.L, w.D)
+    desc = lr.linrec_scan_desc()
+    desc.B, desc.L, desc.D = w.B, w.L, w.D
+    desc.dtype = {"f32": lr.LINREC_F32, "bf16": lr.LINREC_BF16, "f16": lr.LINREC_F16}[dtype]
+    desc.reverse = 0
+    for op in (desc.a, desc.b, desc.h):
+        op.ptr, op.stride_b, op.stride_l = 256, w.L * w.D, w.D
+    plan = lr.linrec_plan()
+    status = lr.library().linrec_scan_ex_plan(ctypes.byref(desc), ctypes.byref(plan))
+    if status != lr.LINREC_OK:
+        raise RuntimeError(f"linrec_scan_ex_plan: {lr.linrec_last_error_message()}")
+    return {name: getattr(plan, name) for name, _ in lr.linrec_plan._fields_}
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, dtype: str = "f32"):
     """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the current kernel source, launch plan and workload; otherwise None."""
-    path = traffic_file(workload)
+    the current kernel source, launch plan, workload and storage type; otherwise None."""
+    path = traffic_file(workload, dtype)
     if not path.exists():
         return None
     rec = json.loads(path.read_text())
     if (rec.get("kernel_source_sha256") != kernel_source_hash() or rec.get("workload") != workload
-            or rec.get("plan") != current_plan(workload)):
+            or rec.get("storage", "f32") != dtype or rec.get("plan") != current_plan(workload, dtype)):
         return None
     return int(rec["hbm_bytes_per_launch"])
 
@@ -92,7 +125,13 @@ def parse_args():
     p.add_argument("--reverse", action="store_true", help="the reverse-time recurrence (linrec_scan_ex)")
     p.add_argument("--state", action="store_true", help="pass an initial state and ask for the final state")
     p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB, at most warmup + steps)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the multi-threaded oracle baseline")
+    p.add_argument("--cpu-single-seconds", type=float, default=5.0, help="time budget of the single-threaded oracle pass")
+    p.add_argument("--cold", type=int, default=0, metavar="N",
+                   help="after the timed steps, N launches each preceded by a cache-evicting write (untimed)")
+    p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
+    p.add_argument("--regions", type=int, default=10,
+                   help="further regions of 10 launches whose means give median/p10/p90 (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibration-copy", type=int, default=0, metavar="N",
                    help="after the timed steps, run N plain device copies of 512 MiB (known bytes) so that "
@@ -122,7 +161,7 @@ def counters_by_kernel(path, counter):
     return out
 
 
-def traffic_record(fetch, write, workload):
+def traffic_record(fetch, write, workload, dtype="f32"):
     """The traffic record from per-dispatch counter bytes (``counters_by_kernel`` of the FETCH_SIZE
     and the WRITE_SIZE run): each counter is scaled by what it reads for a copy of known size."""
     for name, d in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
@@ -133,11 +172,12 @@ def traffic_record(fetch, write, workload):
     read = float(np.mean(fetch["scan"])) * f_factor
     written = float(np.mean(write["scan"])) * w_factor
     w = li.WORKLOADS[workload]
-    algorithmic = 12 * w.elements
+    algorithmic = 3 * STORAGE_BYTES[dtype] * w.elements
     rec = {
         "workload": workload,
+        "storage": dtype,
         "kernel_source_sha256": kernel_source_hash(),
-        "plan": current_plan(workload),
+        "plan": current_plan(workload, dtype),
         "hbm_bytes_per_launch": int(round(read + written)),
         "read_bytes_per_launch": int(round(read)),
         "written_bytes_per_launch": int(round(written)),
@@ -150,20 +190,36 @@ def traffic_record(fetch, write, workload):
     return rec
 
 
-def traffic_from(fetch_csv, write_csv, workload):
+def traffic_from(fetch_csv, write_csv, workload, dtype="f32"):
     """Scale the counters by what they read for a copy of known size; store and print the result."""
     rec = traffic_record(counters_by_kernel(fetch_csv, "FETCH_SIZE"), counters_by_kernel(write_csv, "WRITE_SIZE"),
-                         workload)
-    traffic_file(workload).write_text(json.dumps(rec, indent=1) + "\n")
+                         workload, dtype)
+    traffic_file(workload, dtype).write_text(json.dumps(rec, indent=1) + "\n")
     print(json.dumps(rec))
 
 
-def cpu_baseline(a_np, b_np, h_last, seconds: float, shape, reverse=False, h_init=None):
-    import oracle
+UNIT_ROUNDOFF = {"f32": 0.0, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
 
-    threads = oracle.default_threads()
-    fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
-    n = a_np.size
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
+
+
+def timed_oracle(fn, a_np, b_np, h_init, threads, seconds):
+    """Run the oracle repeatedly for about ``seconds``; returns (passes, elapsed, last result)."""
     passes, ref = 0, None
     t0 = time.perf_counter()
     while True:
@@ -171,26 +227,97 @@ def cpu_baseline(a_np, b_np, h_last, seconds: float, shape, reverse=False, h_ini
         passes += 1
         elapsed = time.perf_counter() - t0
         if elapsed >= seconds:
-            break
+            return passes, elapsed, ref
+
+
+def cpu_baseline(a_np, b_np, h_last, seconds: float, single_seconds: float, shape, storage="f32", reverse=False,
+                 h_init=None):
+    import oracle
+
+    threads = oracle.default_threads()
+    fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
+    n = a_np.size
+    passes, elapsed, ref = timed_oracle(fn, a_np, b_np, h_init, threads, seconds)
     gbs = 12.0 * n * passes / elapsed / 1e9
-    ratio = np.abs(h_last.astype(np.float64) - ref) / (1.0 + np.abs(ref))
+    # the storage type's bar: 1e-4 * (1 + |ref|), plus one rounding to a 16-bit type
+    e = 1e-4 * (1.0 + np.abs(ref))
+    bar = e + UNIT_ROUNDOFF[storage] * (np.abs(ref) + e)
+    ratio = np.abs(h_last.astype(np.float64) - ref) / bar
     B, L, D = shape
-    return {
+    out = {
         "value": round(gbs, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{passes} full passes of the B={B} L={L} D={D} workload in {elapsed:.1f} s "
+        "sample": f"{passes} full passes of the B={B} L={L} D={D} workload in {elapsed:.1f} s on {threads} threads "
                   f"(float64 sequential loop, 12 B/element basis)",
         "elements_per_s": round(n * passes / elapsed, 1),
-        "gpu_check_max_ratio": float(ratio.max()),
+        "host_cores": host_cores(),
+        "cpu_model": cpu_model(),
+        "gpu_check_max_bar_ratio": float(ratio.max()),
+        "gpu_check_bar": "1e-4*(1+|ref|)" + ("" if storage == "f32" else f" plus one {storage} rounding"),
     }
+    if single_seconds > 0:
+        p1, e1, _ = timed_oracle(fn, a_np, b_np, h_init, 1, single_seconds)
+        out["single_thread"] = {
+            "value": round(12.0 * n * p1 / e1 / 1e9, 3),
+            "unit": "GB/s",
+            "elements_per_s": round(n * p1 / e1, 1),
+            "sample": f"{p1} full passes in {e1:.1f} s on 1 thread",
+        }
+    return out
+
+
+def stats_us(samples):
+    x = np.asarray(samples, dtype=np.float64)
+    return {"mean": round(float(x.mean()), 3), "median": round(float(np.median(x)), 3),
+            "p10": round(float(np.percentile(x, 10)), 3), "p90": round(float(np.percentile(x, 90)), 3),
+            "n": int(x.size)}
+
+
+def region_mean_us(torch, launch, count: int, stream, first: int = 0) -> float:
+    """Mean launch time (us) of ``count`` back-to-back calls ``launch(k)`` (k = first, first+1, ...)
+    bracketed by one event pair on ``stream``."""
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record(stream)
+    for k in range(first, first + count):
+        launch(k)
+    e_ev.record(stream)
+    torch.cuda.synchronize()
+    return s_ev.elapsed_time(e_ev) * 1e3 / count
+
+
+def measure_ceiling(torch, xs, ys, zs, rows: int, stream, warmup=3, reps=10):
+    """Best mean launch time (us) of the read-2-write-1 stream over the given buffers (any storage,
+    reinterpreted as float32) for each walk order; returns {order: {...}}."""
+    from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
+
+    flat = lambda t: t.reshape(-1).view(torch.float32)  # noqa: E731
+    X, Y, Z = [flat(t) for t in xs], [flat(t) for t in ys], [flat(t) for t in zs]
+    n = X[0].numel()
+    out = {}
+    for order, r in (("contiguous", 1), ("scan_order", rows)):
+        best = None
+        for unroll in (1, 2, 4):
+            if n % (r * 256 * unroll) != 0:
+                continue
+            for gpc in (1, 2, 4, 8):
+                def launch(k, r=r, unroll=unroll, gpc=gpc):
+                    sc.stream_r2w1(X[k % len(X)], Y[k % len(X)], Z[k % len(X)], r, unroll, gpc, stream)
+                for k in range(warmup):
+                    launch(k)
+                us = region_mean_us(torch, launch, reps, stream, first=warmup)
+                if best is None or us < best["us"]:
+                    best = {"us": round(us, 3), "rows": r, "unroll": unroll, "groups_per_cu": gpc}
+        if best is not None:
+            out[order] = best
+    return out
 
 
 def main():
     args = parse_args()
     if args.traffic_from:
-        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload)
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.workload, args.dtype)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported.  The scan would shard over "
@@ -243,8 +370,8 @@ def main():
         step(i % sets)
     torch.cuda.synchronize()
 
-    # one event pair on the launch stream brackets the timed launches, which run
-    # back to back; their average duration is the region's time over --steps
+    # the timed region: exactly --steps launches back to back, bracketed by one
+    # event pair on the launch stream and by device synchronisation
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -255,18 +382,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     last = (args.warmup + args.steps - 1) % sets
+    # the last output, taken before anything else writes the output buffers
+    h_last = None if args.no_cpu_baseline else h_sets[last].float().cpu().numpy()
+    launch_mean = start.elapsed_time(end) * 1e3 / args.steps
+    launch = {"mean": round(launch_mean, 3)}
+    if args.regions > 0:
+        means = [region_mean_us(torch, lambda k: step(k % sets), 10, stream, first=10 * r) for r in range(args.regions)]
+        spread = stats_us(means)
+        launch.update(median=spread["median"], p10=spread["p10"], p90=spread["p90"],
+                      spread_of="means of %d further regions of 10 back-to-back launches" % args.regions)
 
-    launch_us = start.elapsed_time(end) * 1e3 / args.steps
     ms_per_step = wall * 1e3 / args.steps
     value = step_bytes / (wall / args.steps) / 1e9
-    achieved = step_bytes / (launch_us * 1e-6) / 1e9
+    achieved = step_bytes / (launch_mean * 1e-6) / 1e9
 
-    variant = "" if plain else " (linrec_scan_ex: " + ", ".join(
-        x for x in (f"{args.dtype} storage" if args.dtype != "f32" else "", "reverse time" if args.reverse else "",
-                    "initial and final state" if args.state else "") if x) + ")"
+    storage_name = {"f32": "fp32", "bf16": "bf16", "f16": "fp16"}[args.dtype]
+    variant = "" if plain else " (linrec_scan_ex" + "".join(
+        ", " + x for x in ("reverse time" if args.reverse else "", "initial and final state" if args.state else "")
+        if x) + ")"
     headline = args.workload == li.HEADLINE and plain
+    desc = w.describe(storage_name + ("" if args.dtype == "f32" else " storage, fp32 arithmetic"))
     out = {
-        "metric": METRIC if headline else f"achieved HBM GB/s, linrec_scan {w.describe()}{variant}",
+        "metric": METRIC if headline else f"achieved HBM GB/s, linrec_scan {desc}{variant}",
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -279,26 +416,50 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: {w.describe()}{variant}",
+            "workload": f"{args.workload}: {desc}{variant}",
             "B": w.B, "L": w.L, "D": w.D, "seed": seed,
-            "storage": args.dtype, "reverse": args.reverse, "state": args.state,
+            "storage": args.dtype, "arithmetic": "fp32 (fp64 products of decays on the carry path)",
+            "reverse": args.reverse, "state": args.state,
             "algorithmic_bytes_per_step": step_bytes,
             "buffer_sets": sets,
             "plan": plan,
         },
         "frac_of_peak": round(value / PEAK_HBM_GBS, 4),
         "elements_per_s": round(n / (wall / args.steps), 1),
-        "launch_us_mean": round(launch_us, 2),
+        "launch_us": launch,
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(args.workload) if plain else None,
+            "traffic": measured_traffic(args.workload, args.dtype) if not (args.reverse or args.state) else None,
         },
+        "ceiling_gbs": None,
+        "frac_of_ceiling": None,
+        "ceiling": None,
         "cpu_baseline": None,
     }
+    if not args.no_ceiling:
+        ceil = measure_ceiling(torch, a_sets, b_sets, h_sets, w.B, stream)
+        for v in ceil.values():
+            v["gbs"] = round(3 * elem * n / (v["us"] * 1e-6) / 1e9, 1)
+        out["ceiling"] = dict(ceil, kind="read-2-write-1 stream z = x + y (libstream_ceiling.so) over the same "
+                                          "buffers; best mean launch time over unroll x groups_per_cu")
+        if "contiguous" in ceil:
+            out["ceiling_gbs"] = ceil["contiguous"]["gbs"]
+            out["frac_of_ceiling"] = round(achieved / ceil["contiguous"]["gbs"], 4) if not args.state else None
+    if args.cold > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        cold, warm = [], []
+        for i in range(args.cold):
+            for evict, into in ((True, cold), (False, warm)):
+                if evict:
+                    flush.fill_(float(i))
+                into.append(region_mean_us(torch, lambda k: step(k % sets), 1, stream, first=i))
+        del flush
+        out["single_launch_us"] = {"cold": stats_us(cold), "warm": stats_us(warm),
+                                   "note": "one event pair per launch (adds its own overhead to both)"}
     if args.calibration_copy:
         src = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -308,9 +469,9 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         # the oracle on the values the GPU consumed (16-bit inputs widen exactly)
-        h_last = h_sets[last].float().cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(a_host.float().numpy(), b_host.float().numpy(), h_last, args.cpu_seconds,
-                                           (w.B, w.L, w.D), reverse=args.reverse, h_init=h0_np)
+                                           args.cpu_single_seconds, (w.B, w.L, w.D), storage=args.dtype,
+                                           reverse=args.reverse, h_init=h0_np)
     print(json.dumps(out), flush=True)
 
 

@@ -49,13 +49,15 @@ class Workload:
     def elements(self) -> int:
         return self.B * self.L * self.D
 
-    def describe(self) -> str:
+    def describe(self, storage: str = "fp32") -> str:
+        """Shape, storage type and distributions; ``storage`` names the type a, b and h are held
+        in (the values are drawn in fp32 and, for 16-bit storage, rounded to it)."""
         if self.a_dist == "normal":
             a = "a~N(0,1)"
         else:
             a = f"a~U({self.a_lo:g},{self.a_hi:g})"
         extra = f", {self.reset:.0%} resets a=0" if self.reset else ""
-        return f"B={self.B} L={self.L} D={self.D} fp32, {a}, b~N(0,1){extra}"
+        return f"B={self.B} L={self.L} D={self.D} {storage}, {a}, b~N(0,1){extra}"
 
 
 WORKLOADS = {

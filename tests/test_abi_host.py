@@ -10,12 +10,14 @@ import pytest
 
 from linear_recurrence_scan_linrec_amd import linrec as binding
 
-HEADER = Path(__file__).resolve().parent.parent / "include" / "linrec.h"
+INCLUDE = Path(__file__).resolve().parent.parent / "include"
+HEADER = INCLUDE / "linrec.h"
+STREAM_HEADER = INCLUDE / "linrec_stream.h"
 
 
-def declared_functions():
-    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
-    return sorted(set(re.findall(r"\b(linrec_[a-z_]+)\s*\(", text)))
+def declared_functions(header=HEADER):
+    text = re.sub(r"/\*.*?\*/", "", header.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(linrec_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -25,6 +27,33 @@ def test_every_declared_symbol_is_exported():
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, f"declared but not exported: {missing}"
     assert sorted(binding.EXPORTED) == names
+
+
+def test_every_header_is_covered():
+    """Each header under include/ belongs to one of the two libraries checked here."""
+    assert sorted(p.name for p in INCLUDE.glob("*.h")) == ["linrec.h", "linrec_stream.h"]
+
+
+def test_stream_ceiling_library_exports_and_checks_arguments():
+    from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
+
+    names = declared_functions(STREAM_HEADER)
+    lib = sc.library()
+    assert names == sorted(sc.EXPORTED) and all(hasattr(lib, n) for n in names)
+    f = lib.linrec_stream_r2w1
+    # checks that return before any HIP call
+    assert f(None, None, None, 0, 1, 4, 2, None) == 0                       # empty: no-op
+    assert f(None, None, None, 1024, 1, 3, 2, None) == 1                    # unroll
+    assert b"unroll" in lib.linrec_stream_last_error()
+    assert f(None, None, None, 1024, 1, 4, 0, None) == 1                    # groups per CU
+    assert f(None, None, None, 1000, 1, 1, 2, None) == 1                    # not whole segments
+    assert f(None, None, None, 1024, 3, 1, 2, None) == 1                    # rows do not divide it
+    assert f(None, None, None, 1024, 1, 1, 2, None) == 1                    # null buffers
+    base = 1 << 32
+    assert f(base, base + 8192, base + 16, 1024, 1, 1, 2, None) == 1         # z overlaps x
+    assert b"overlaps" in lib.linrec_stream_last_error()
+    assert f(base + 4, base + 8192, base + 65536, 1024, 1, 1, 2, None) == 1  # misaligned
+    assert b"aligned" in lib.linrec_stream_last_error()
 
 
 def test_status_strings():

@@ -10,7 +10,8 @@ pytestmark = pytest.mark.gpu
 
 
 def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline(monkeypatch, capsys):
-    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.05"])
+    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", "--cpu-seconds", "0.05",
+                                     "--cpu-single-seconds", "0.05", "--cold", "2"])
     print("bench.main: pages_shape, 3 steps", flush=True)
     bench.main()
     lines = [line for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
@@ -29,24 +30,48 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline(monkeypatc
     assert 0 < roof["achieved"] <= roof["peak"]
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-4)
     assert roof["traffic"] == bench.measured_traffic("pages_shape")
+    launch = r["launch_us"]
+    assert launch["p10"] <= launch["median"] <= launch["p90"] and "10 further regions" in launch["spread_of"]
+    assert roof["achieved"] == pytest.approx(r["config"]["algorithmic_bytes_per_step"] / launch["mean"] / 1e3, rel=1e-3)
+    # the streaming ceiling over the same bytes, both walk orders, and the scan's share of it
+    ceil = r["ceiling"]
+    assert ceil["contiguous"]["rows"] == 1 and ceil["scan_order"]["rows"] == 32
+    assert r["ceiling_gbs"] == ceil["contiguous"]["gbs"] > 0
+    assert r["frac_of_ceiling"] == pytest.approx(roof["achieved"] / r["ceiling_gbs"], abs=1e-3)
+    single = r["single_launch_us"]
+    assert single["cold"]["n"] == 2 and single["warm"]["n"] == 2 and single["cold"]["mean"] > 0
     cpu = r["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["unit"] == "GB/s" and cpu["value"] > 0 and cpu["cores"] >= 1
+    assert cpu["host_cores"] >= cpu["cores"] and cpu["cpu_model"]
+    assert cpu["single_thread"]["value"] > 0
     assert isinstance(cpu["sample"], str) and cpu["sample"]
     # the oracle's answer for the GPU's last output, within the parity bar
-    assert cpu["gpu_check_max_ratio"] <= 1e-4
+    assert cpu["gpu_check_max_bar_ratio"] <= 1.0
 
 
-@pytest.mark.parametrize("extra,workload", [(["--workload", "tiny"], "tiny"),
-                                            (["--dtype", "bf16", "--reverse", "--state"], "pages_shape")],
-                         ids=["tiny", "bf16_reverse_state"])
+@pytest.mark.parametrize("extra,workload", [(["--workload", "tiny", "--no-cpu-baseline"], "tiny"),
+                                            (["--dtype", "bf16", "--reverse", "--state", "--no-cpu-baseline"],
+                                             "pages_shape"),
+                                            (["--dtype", "bf16", "--cpu-seconds", "0.05",
+                                              "--cpu-single-seconds", "0"], "pages_shape")],
+                         ids=["tiny", "bf16_reverse_state", "bf16_checked"])
 def test_bench_other_workloads_and_forms(monkeypatch, capsys, extra, workload):
-    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", "--no-cpu-baseline", *extra])
+    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", *extra])
     print(f"bench.main: {' '.join(extra)}", flush=True)
     bench.main()
     lines = [line for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
     assert len(lines) == 1
     r = json.loads(lines[0])
-    assert r["config"]["workload"].startswith(workload) and r["value"] > 0 and r["cpu_baseline"] is None
+    assert r["config"]["workload"].startswith(workload) and r["value"] > 0
     assert r["roofline"]["bound"] == "hbm" and r["roofline"]["achieved"] > 0
-    plain = workload != "pages_shape"   # the second case runs through linrec_scan_ex
-    assert r["roofline"]["traffic"] == (bench.measured_traffic(workload) if plain else None)
+    # a counter record applies to forward scans without states of the same workload and storage
+    forward = "--reverse" not in extra and "--state" not in extra
+    dtype = r["config"]["storage"]
+    assert r["roofline"]["traffic"] == (bench.measured_traffic(workload, dtype) if forward else None)
+    if "bf16" in extra:
+        assert r["config"]["storage"] == "bf16" and "bf16 storage" in r["config"]["workload"]
+    if "--no-cpu-baseline" in extra:
+        assert r["cpu_baseline"] is None
+    else:
+        # a 16-bit output checked against the bar with one bf16 rounding
+        assert r["cpu_baseline"]["gpu_check_max_bar_ratio"] <= 1.0 and "single_thread" not in r["cpu_baseline"]

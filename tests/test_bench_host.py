@@ -36,6 +36,15 @@ def test_counters_by_kernel_keeps_scan_and_copy_rows_in_bytes(tmp_path):
 def test_traffic_file_is_named_for_the_planned_kernel():
     assert bench.traffic_file("pages_shape").name == "traffic_scan_tiles_pages_shape.json"
     assert bench.traffic_file("long_sequence").name == "traffic_scan_one_long_sequence.json"
+    assert bench.traffic_file("pages_shape", "bf16").name == "traffic_scan_one_pages_shape_bf16.json"
+    assert bench.traffic_file("near_unit_resets", "f16").name == "traffic_scan_tiles_near_unit_resets_f16.json"
+
+
+def test_current_plan_of_fp32_matches_the_plain_entry_point():
+    from linear_recurrence_scan_linrec_amd import linrec as lr
+
+    for name, w in bench.li.WORKLOADS.items():
+        assert bench.current_plan(name) == lr.linrec_scan_plan(w.B, w.L, w.D), name
 
 
 def test_traffic_record_scales_by_the_calibration_copy():
@@ -50,6 +59,10 @@ def test_traffic_record_scales_by_the_calibration_copy():
     assert rec["algorithmic_bytes_per_launch"] == 12 * 32 * 4096 * 256
     assert rec["scan_dispatches"] == [2, 2] and rec["copy_dispatches"] == [3, 3]
     assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
+    assert rec["storage"] == "f32"
+    rec16 = bench.traffic_record(fetch, write, "pages_shape", "bf16")
+    assert rec16["algorithmic_bytes_per_launch"] == 6 * 32 * 4096 * 256 and rec16["storage"] == "bf16"
+    assert rec16["plan"] == bench.current_plan("pages_shape", "bf16")
 
 
 def test_traffic_record_needs_both_kernels():
@@ -70,7 +83,7 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path, monkeypatch):
 
 def test_measured_traffic_applies_only_to_the_same_kernel_plan_and_workload(tmp_path, monkeypatch):
     record = tmp_path / "traffic.json"
-    monkeypatch.setattr(bench, "traffic_file", lambda workload: record)
+    monkeypatch.setattr(bench, "traffic_file", lambda workload, dtype="f32": record)
     rec = {"workload": "pages_shape", "kernel_source_sha256": bench.kernel_source_hash(),
            "plan": bench.current_plan("pages_shape"), "hbm_bytes_per_launch": 403000000}
     record.write_text(json.dumps(rec))
@@ -81,6 +94,7 @@ def test_measured_traffic_applies_only_to_the_same_kernel_plan_and_workload(tmp_
     assert bench.measured_traffic("pages_shape") is None
     record.write_text(json.dumps(rec))
     assert bench.measured_traffic("wide_channels") is None
+    assert bench.measured_traffic("pages_shape", "bf16") is None     # a record of fp32 storage
 
 
 def test_more_than_one_gpu_exits_with_a_message_before_touching_a_device(monkeypatch, capsys):
