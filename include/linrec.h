@@ -60,21 +60,30 @@ typedef enum linrec_status {
  * least B*L*D*4 bytes (checked with the HIP runtime before launch).
  *
  * Workspace: when L spans several tiles and the tiles must look back across
- * workgroups, the call uses a per-device workspace that the library
- * allocates on first need (hipMalloc, outside any stream), grows when a
- * larger shape needs more, and frees in linrec_release().  Calls on one
- * device share it, so calls that may overlap in time on one device must be
- * ordered on one stream; calls on different streams of one device race.
- * When the persistent workgroups can take whole (batch row, channel slab)
- * sequences, 1 to 4 each, the carry stays inside each workgroup and the call
- * touches no workspace.
+ * workgroups, the call uses a workspace of status words.  The library keeps
+ * one per (device, stream): it allocates it on the first call on that stream
+ * that needs one (hipMalloc and a clear, outside any stream), replaces it with
+ * a larger one when a shape needs more, and frees all of them in
+ * linrec_release().  A replaced workspace is kept, not freed, until then (a
+ * graph captured with it may still be replayed).  Calls on one stream are
+ * ordered, and calls on different streams use different workspaces, so
+ * concurrent streams never share status words.  Each stream that makes such
+ * calls holds its own workspace (a few MB for shapes like B=2 L=262144 D=64)
+ * until linrec_release().  linrec_scan_ws takes the workspace from the caller
+ * instead.  When the persistent workgroups can take whole (batch row, channel
+ * slab) sequences, 1 to 4 each, the carry stays inside each workgroup and the
+ * call touches no workspace.
  *
  * Graph capture: a call enqueues kernel launches only (no memset, no copy), so
  * it can be captured into a HIP graph and replayed, provided the workspace it
- * needs already exists -- make one call of the same or a larger shape on the
- * device before capturing, since allocating is not allowed while capturing.
- * Replays need no host work between them: each call's lookback epoch advances
- * inside the kernel.
+ * needs already exists: make one call of the same or a larger shape on the
+ * capturing stream before capturing (a call that would have to allocate while
+ * its stream is captured returns LINREC_ERR_INVALID_ARGUMENT), or pass a
+ * workspace to linrec_scan_ws.  Replays need no host work between them: each
+ * call's lookback epoch advances inside the kernel.  A captured call keeps
+ * using the workspace it was captured with, so a replay must be ordered with
+ * the other calls that use that workspace (those on the stream it was
+ * captured on).
  *
  * Alignment: buffers must be aligned to 4 bytes (any fp32 array is): 16-byte
  * aligned buffers with D % 4 == 0 use 128-bit accesses, anything else the
@@ -206,6 +215,44 @@ linrec_status linrec_scan_ex(const linrec_scan_desc *desc, void *stream);
  * buffers are not checked). */
 linrec_status linrec_scan_ex_plan(const linrec_scan_desc *desc, linrec_plan *plan);
 
+/*
+ * Caller-provided workspaces -- for callers that run scans concurrently on
+ * several streams of one device and want to manage the memory themselves, or
+ * that capture graphs without a warm-up call.  Same operation, arguments,
+ * ownership, errors and environment as linrec_scan / linrec_scan_ex, except
+ * that the lookback workspace (see "Workspace" above) is the caller's:
+ *
+ *   workspace        device memory of the current device, 256-byte aligned,
+ *                    at least the bytes the *_workspace_bytes functions give,
+ *                    overlapping no operand, and ZERO-FILLED before its first
+ *                    use (e.g. hipMemset).  The library keeps it consistent
+ *                    from call to call afterwards (every 2^29 calls on one
+ *                    workspace, a call also enqueues a clear of it on its
+ *                    stream).  It may serve calls of any shape.
+ *   workspace_bytes  its size.  May be anything (workspace may be NULL) when
+ *                    the call needs no workspace.
+ *
+ * Calls that share one workspace must be ordered (one stream, or events);
+ * calls with different workspaces may run concurrently.  These entry points
+ * never allocate.  LINREC_ERR_INVALID_ARGUMENT when a needed workspace is
+ * missing, too small, misaligned or not device memory of the current device;
+ * LINREC_ERR_OVERLAP when it overlaps an operand.
+ */
+linrec_status linrec_scan_ws(const float *a, const float *b, float *h, int64_t B, int64_t L, int64_t D,
+                             void *workspace, size_t workspace_bytes, void *stream);
+linrec_status linrec_scan_ex_ws(const linrec_scan_desc *desc, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/* Workspace bytes a linrec_scan_ws call of shape (B, L, D) may need on the
+ * current device, whatever the buffers' alignment (0: none, or invalid
+ * sizes).  Host arithmetic plus a query of the device's CU count. */
+size_t linrec_scan_workspace_bytes(int64_t B, int64_t L, int64_t D);
+
+/* Workspace bytes linrec_scan_ex_ws(desc) may need on the current device, into
+ * *bytes (0: none).  LINREC_ERR_INVALID_ARGUMENT for a null bytes or an
+ * invalid desc (the checks of linrec_scan_ex_plan). */
+linrec_status linrec_scan_ex_workspace_bytes(const linrec_scan_desc *desc, size_t *bytes);
+
 /* Static English text for a status code; "unknown status" for other values. */
 const char *linrec_status_string(int status);
 
@@ -214,22 +261,24 @@ const char *linrec_status_string(int status);
 const char *linrec_last_error_message(void);
 
 /*
- * linrec_device_timeouts -- on the current device, since the workspace was
- * allocated: how many lookback wavefronts (at most four per workgroup per
- * call) stopped waiting for a predecessor's published carry at least once and
- * recomputed that predecessor's pair from the inputs instead.  The output is
+ * linrec_device_timeouts -- on the current device, summed over the library's
+ * own workspaces since each was allocated (caller-provided workspaces keep
+ * their own count): how many lookback wavefronts (at most four per workgroup
+ * per call) stopped waiting for a predecessor's published carry at least once
+ * and recomputed that predecessor's pair from the inputs instead.  The output is
  * correct either way; the count shows how often the cross-workgroup wait ran
  * out (normally 0).  Synchronises the device before reading.  Returns
  * LINREC_OK and stores the count in *count (0 when no workspace exists).
  */
 linrec_status linrec_device_timeouts(uint64_t *count);
 
-/* Frees the per-device workspaces, synchronising each device that holds one
- * first.  No other thread may call into the library meanwhile.  A HIP graph
- * that captured a call whose tiles look back refers to the freed workspace:
- * do not replay it after linrec_release (capture it again after a first call
+/* Frees the library's workspaces (those of every stream, and the ones larger
+ * shapes replaced), synchronising each device that holds one first.  No other
+ * thread may call into the library meanwhile.  A HIP graph that captured a
+ * call whose tiles look back through a library workspace refers to freed
+ * memory afterwards: do not replay it (capture it again after a first call
  * has allocated a new workspace).  The next call that needs a workspace
- * allocates a new one. */
+ * allocates a new one.  Caller-provided workspaces are not touched. */
 void linrec_release(void);
 
 #ifdef __cplusplus

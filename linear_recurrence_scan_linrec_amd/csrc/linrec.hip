@@ -18,6 +18,8 @@
 #include <mutex>
 #include <string>
 #include <tuple>
+#include <utility>
+#include <vector>
 
 // Zero-fill used to (re)initialise a workspace; a kernel rather than a memset
 // so that it can sit inside captured graphs.
@@ -459,18 +461,30 @@ linrec_status resident_groups(int device, const Launch* l, int threads, int64_t&
 
 // ----------------------------------------------------------------------------- workspace
 
-// The epoch in the status tags has 30 bits; clearing the workspace every 2^29
+// The epoch in the status tags has 30 bits; clearing a workspace every 2^29
 // calls keeps a stale word from ever carrying the current epoch.
 constexpr uint64_t kClearPeriod = 1ull << 29;
+// Alignment asked of a caller's workspace (its header and slot lines are
+// 128-byte lines; the status words are 64-bit atomics).
+constexpr uintptr_t kWorkspaceAlign = 256;
 
-struct DeviceWorkspace {
+struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
     uint64_t calls = 0;
 };
 
+// Library-owned workspaces, one per (device, stream): calls on one stream are
+// ordered, which the in-kernel epoch advance relies on, and calls on
+// different streams never share status words.  A workspace that a larger
+// shape outgrows is retired, not freed: graphs captured with it may still be
+// replayed, and work enqueued with it may still be running.  linrec_release
+// frees both kinds.
 std::mutex g_mutex;
-std::map<int, DeviceWorkspace> g_workspaces;
+std::map<std::pair<int, void*>, Workspace> g_workspaces;
+std::vector<std::pair<int, void*>> g_retired;   // (device, pointer)
+// calls per caller-provided workspace, for the periodic clear
+std::map<std::pair<int, void*>, uint64_t> g_caller_calls;
 
 unsigned grid_for(int64_t n) {
     const int64_t blocks = (n + 255) / 256;
@@ -486,19 +500,29 @@ linrec_status zero_fill(void* p, size_t bytes, hipStream_t stream) {
     return LINREC_OK;
 }
 
-// Returns the device workspace of at least `need` bytes, allocating or growing it.
+// True when `stream` is being captured into a graph (then nothing may be allocated).
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus status = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &status) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return status != hipStreamCaptureStatusNone;
+}
+
+// The library's workspace of `stream` on `device`, at least `need` bytes:
+// allocated (and cleared) on first need, replaced by a larger one when a shape
+// needs more.
 linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, void*& out) {
     std::lock_guard<std::mutex> lock(g_mutex);
-    DeviceWorkspace& ws = g_workspaces[device];
+    Workspace& ws = g_workspaces[std::make_pair(device, static_cast<void*>(stream))];
     if (ws.bytes < need) {
-        if (ws.ptr != nullptr) {
-            // the old workspace may still be in use by enqueued work
-            hipError_t e = hipDeviceSynchronize();
-            if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipDeviceSynchronize before growing the workspace: " + hip_text(e));
-            e = hipFree(ws.ptr);
-            ws = DeviceWorkspace{};
-            if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipFree of the old workspace: " + hip_text(e));
-        }
+        if (capturing(stream))
+            return fail(LINREC_ERR_INVALID_ARGUMENT,
+                        "the call needs a lookback workspace of " + std::to_string(need) +
+                            " bytes on this stream and the stream is being captured, where nothing may be "
+                            "allocated: make one call of this or a larger shape on the stream before capturing, "
+                            "or pass a workspace (linrec_scan_ws / linrec_scan_ex_ws)");
         const size_t mib = size_t(1) << 20;
         const size_t bytes = (need + need / 4 + mib - 1) / mib * mib;
         void* p = nullptr;
@@ -512,9 +536,8 @@ linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, voi
             (void)hipFree(p);
             return fail(LINREC_ERR_HIP, "clearing the new workspace: " + hip_text(e));
         }
-        ws.ptr = p;
-        ws.bytes = bytes;
-        ws.calls = 0;
+        if (ws.ptr != nullptr) g_retired.emplace_back(device, ws.ptr);
+        ws = Workspace{p, bytes, 0};
     }
     ws.calls += 1;
     if (ws.calls % kClearPeriod == 0) {
@@ -522,6 +545,16 @@ linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, voi
         if (s != LINREC_OK) return s;
     }
     out = ws.ptr;
+    return LINREC_OK;
+}
+
+// A caller's workspace: counted for the periodic clear, which this call then
+// enqueues on `stream` (never allocated or freed here).
+linrec_status use_caller_workspace(int device, void* ptr, size_t bytes, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    uint64_t& calls = g_caller_calls[std::make_pair(device, ptr)];
+    calls += 1;
+    if (calls % kClearPeriod == 0) return zero_fill(ptr, bytes, stream);
     return LINREC_OK;
 }
 
@@ -560,7 +593,14 @@ bool overlaps(const void* x, int64_t xbytes, const void* y, int64_t ybytes) {
     return a < b + static_cast<uintptr_t>(ybytes) && b < a + static_cast<uintptr_t>(xbytes);
 }
 
-linrec_status run_scan(const Problem& pr, void* stream) {
+// Where a call's lookback workspace comes from.
+struct WorkspaceSource {
+    bool caller = false;   // true: the caller's (ptr, bytes), possibly null; false: the library's own
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& src = WorkspaceSource{}) {
     const linrec_scan_desc& q = pr.desc;
     const int64_t states = q.B * q.D;
     const int64_t state_bytes = states * static_cast<int64_t>(sizeof(float));
@@ -623,8 +663,25 @@ linrec_status run_scan(const Problem& pr, void* stream) {
     }
     void* ws = nullptr;
     if (p.workspace_bytes > 0 && p.geom.local_seqs == 0) {
-        s = acquire_workspace(device, p.workspace_bytes, hs, ws);
-        if (s != LINREC_OK) return s;
+        if (src.caller) {
+            if (src.ptr == nullptr || src.bytes < p.workspace_bytes)
+                return fail(LINREC_ERR_INVALID_ARGUMENT,
+                            "this call needs a workspace of " + std::to_string(p.workspace_bytes) + " bytes, got " +
+                                std::to_string(src.ptr == nullptr ? 0 : src.bytes));
+            if (reinterpret_cast<uintptr_t>(src.ptr) % kWorkspaceAlign != 0)
+                return fail(LINREC_ERR_INVALID_ARGUMENT, "the workspace must be aligned to 256 bytes");
+            const int64_t wb = static_cast<int64_t>(src.bytes);
+            if (overlaps(src.ptr, wb, q.a.ptr, pr.extent_a) || overlaps(src.ptr, wb, q.b.ptr, pr.extent_b) ||
+                overlaps(src.ptr, wb, q.h.ptr, pr.extent_h) || overlaps(src.ptr, wb, q.h_init, state_bytes) ||
+                overlaps(src.ptr, wb, q.h_final, state_bytes))
+                return fail(LINREC_ERR_OVERLAP, "the workspace overlaps another buffer");
+            if ((s = check_buffer(src.ptr, wb, device, "workspace")) != LINREC_OK) return s;
+            if ((s = use_caller_workspace(device, src.ptr, src.bytes, hs)) != LINREC_OK) return s;
+            ws = src.ptr;
+        } else {
+            s = acquire_workspace(device, p.workspace_bytes, hs, ws);
+            if (s != LINREC_OK) return s;
+        }
     }
     WorkspaceHeader* hdr = static_cast<WorkspaceHeader*>(ws);
     uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader) +
@@ -657,6 +714,29 @@ linrec_scan_desc contiguous_f32(const float* a, const float* b, float* h, int64_
 bool size_ok(int64_t B, int64_t L, int64_t D) {
     int64_t bl = 0, n = 0;
     return B >= 0 && L >= 0 && D >= 0 && checked_mul(B, L, bl) && checked_mul(bl, D, n) && n <= INT64_MAX / 8;
+}
+
+// CUs of the current device, or the plan entry points' assumption when there is none.
+int current_cus() {
+    int device = 0, cus = 0;
+    if (hipGetDevice(&device) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus < 1) {
+        (void)hipGetLastError();
+        return kPlanCus;
+    }
+    return cus;
+}
+
+// Lookback workspace bytes a call of this problem may need on the current device (0: none).
+linrec_status workspace_need(const linrec_scan_desc* desc, size_t& bytes) {
+    bytes = 0;
+    Problem pr;
+    linrec_status s = make_problem(desc, pr);
+    if (s != LINREC_OK) return s;
+    Plan p;
+    if ((s = make_plan(pr, p, current_cus())) != LINREC_OK) return s;
+    bytes = p.workspace_bytes;
+    return LINREC_OK;
 }
 
 }  // namespace
@@ -699,6 +779,45 @@ linrec_status linrec_scan_ex(const linrec_scan_desc* desc, void* stream) {
     return run_scan(pr, stream);
 }
 
+size_t linrec_scan_workspace_bytes(int64_t B, int64_t L, int64_t D) {
+    if (!size_ok(B, L, D)) return 0;
+    size_t most = 0;
+    // the plan follows the buffers' alignment: take the larger of the two
+    for (uintptr_t base : {uintptr_t(256), uintptr_t(260)}) {
+        const float* f = reinterpret_cast<const float*>(base);
+        const linrec_scan_desc d = contiguous_f32(f, f, const_cast<float*>(f), B, L, D);
+        size_t bytes = 0;
+        if (workspace_need(&d, bytes) == LINREC_OK) most = std::max(most, bytes);
+    }
+    return most;
+}
+
+linrec_status linrec_scan_ex_workspace_bytes(const linrec_scan_desc* desc, size_t* bytes) {
+    if (bytes == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "bytes is null");
+    return workspace_need(desc, *bytes);
+}
+
+linrec_status linrec_scan_ws(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    t_last_error.clear();
+    if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
+    if (B == 0 || L == 0 || D == 0) return LINREC_OK;
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
+    const linrec_scan_desc d = contiguous_f32(a, b, h, B, L, D);
+    Problem pr;
+    const linrec_status s = make_problem(&d, pr);
+    if (s != LINREC_OK) return s;
+    return run_scan(pr, stream, WorkspaceSource{true, workspace, workspace_bytes});
+}
+
+linrec_status linrec_scan_ex_ws(const linrec_scan_desc* desc, void* workspace, size_t workspace_bytes, void* stream) {
+    t_last_error.clear();
+    Problem pr;
+    const linrec_status s = make_problem(desc, pr);
+    if (s != LINREC_OK) return s;
+    return run_scan(pr, stream, WorkspaceSource{true, workspace, workspace_bytes});
+}
+
 linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D, void* stream) {
     t_last_error.clear();
     if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
@@ -730,19 +849,23 @@ linrec_status linrec_device_timeouts(uint64_t* count) {
     int device = 0;
     hipError_t e = hipGetDevice(&device);
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipGetDevice: " + hip_text(e));
-    void* ptr = nullptr;
+    std::vector<void*> ptrs;
     {
         std::lock_guard<std::mutex> lock(g_mutex);
-        auto it = g_workspaces.find(device);
-        if (it != g_workspaces.end()) ptr = it->second.ptr;
+        for (const auto& kv : g_workspaces)
+            if (kv.first.first == device && kv.second.ptr != nullptr) ptrs.push_back(kv.second.ptr);
+        for (const auto& r : g_retired)
+            if (r.first == device) ptrs.push_back(r.second);
     }
-    if (ptr == nullptr) return LINREC_OK;
+    if (ptrs.empty()) return LINREC_OK;
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "hipDeviceSynchronize: " + hip_text(e));
-    WorkspaceHeader hdr;
-    e = hipMemcpy(&hdr, ptr, sizeof(hdr), hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return fail(LINREC_ERR_HIP, "reading the workspace header: " + hip_text(e));
-    *count = hdr.timeouts;
+    for (void* ptr : ptrs) {
+        WorkspaceHeader hdr;
+        e = hipMemcpy(&hdr, ptr, sizeof(hdr), hipMemcpyDeviceToHost);
+        if (e != hipSuccess) return fail(LINREC_ERR_HIP, "reading a workspace header: " + hip_text(e));
+        *count += hdr.timeouts;
+    }
     return LINREC_OK;
 }
 
@@ -750,14 +873,20 @@ void linrec_release(void) {
     std::lock_guard<std::mutex> lock(g_mutex);
     int current = 0;
     const bool have_current = hipGetDevice(&current) == hipSuccess;
-    for (auto& kv : g_workspaces) {
-        if (kv.second.ptr == nullptr) continue;
-        if (hipSetDevice(kv.first) == hipSuccess) {
+    std::vector<std::pair<int, void*>> all(g_retired);
+    for (const auto& kv : g_workspaces)
+        if (kv.second.ptr != nullptr) all.emplace_back(kv.first.first, kv.second.ptr);
+    std::map<int, bool> synced;
+    for (const auto& w : all) {
+        if (hipSetDevice(w.first) != hipSuccess) continue;
+        if (!synced[w.first]) {
             (void)hipDeviceSynchronize();
-            (void)hipFree(kv.second.ptr);
+            synced[w.first] = true;
         }
+        (void)hipFree(w.second);
     }
     g_workspaces.clear();
+    g_retired.clear();
     if (have_current) (void)hipSetDevice(current);
     (void)hipGetLastError();
 }

@@ -35,6 +35,10 @@ EXPORTED = (
     "linrec_last_error_message",
     "linrec_device_timeouts",
     "linrec_release",
+    "linrec_scan_ws",
+    "linrec_scan_ex_ws",
+    "linrec_scan_workspace_bytes",
+    "linrec_scan_ex_workspace_bytes",
 )
 
 
@@ -109,6 +113,14 @@ def _load() -> ctypes.CDLL:
     lib.linrec_device_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint64)]
     lib.linrec_release.restype = None
     lib.linrec_release.argtypes = []
+    lib.linrec_scan_ws.restype = ctypes.c_int
+    lib.linrec_scan_ws.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.c_size_t, vp]
+    lib.linrec_scan_ex_ws.restype = ctypes.c_int
+    lib.linrec_scan_ex_ws.argtypes = [ctypes.POINTER(linrec_scan_desc), vp, ctypes.c_size_t, vp]
+    lib.linrec_scan_workspace_bytes.restype = ctypes.c_size_t
+    lib.linrec_scan_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.linrec_scan_ex_workspace_bytes.restype = ctypes.c_int
+    lib.linrec_scan_ex_workspace_bytes.argtypes = [ctypes.POINTER(linrec_scan_desc), ctypes.POINTER(ctypes.c_size_t)]
     return lib
 
 
@@ -189,8 +201,17 @@ def _stream_ptr(stream, index: int) -> int:
     return torch.cuda.current_stream(index).cuda_stream
 
 
-def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr):
-    if plain:
+def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr, workspace):
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if plain:
+            B, L, D = a.size()
+            _check(_lib.linrec_scan_ws(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, ws_ptr, ws_bytes,
+                                       stream_ptr))
+        else:
+            desc = make_desc(a, b, h, h_init, h_final, reverse)
+            _check(_lib.linrec_scan_ex_ws(ctypes.byref(desc), ws_ptr, ws_bytes, stream_ptr))
+    elif plain:
         B, L, D = a.size()
         _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, stream_ptr))
     else:
@@ -198,7 +219,8 @@ def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr):
         _check(_lib.linrec_scan_ex(ctypes.byref(desc), stream_ptr))
 
 
-def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_final=False, reverse=False):
+def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_final=False, reverse=False,
+                workspace=None):
     """The channel-wise linear recurrence on the GPU.
 
     Forward (default): h[i,0,d] = a[i,0,d]*h_init[i,d] + b[i,0,d] (h_init taken as 0 when
@@ -213,6 +235,14 @@ def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_
     tensor that receives the state after the last step (allocated when ``return_final``).
     Returns ``h``, or ``(h, h_final)`` when a final state is asked for.  The call is enqueued on
     ``stream`` (default: the current stream of a's device) and returns without synchronising.
+    ``workspace`` (optional): a zero-filled CUDA tensor on a's device, 256-byte aligned, of at least
+    ``workspace_bytes(...)`` bytes, used as the lookback workspace instead of the library's own
+    for the stream (linrec_scan_ws / linrec_scan_ex_ws).
+
+    Under CUDA-graph capture of the current stream (``torch.cuda.graph``), a call that needs a
+    lookback workspace and is given none gets one from the graph's memory pool, zero-filled by a
+    fill kernel recorded in the graph before the scan, so that every replay starts from a clean
+    workspace (the library itself never allocates while a stream is captured).
     """
     like = _check_operand("a", a)
     _check_operand("b", b, like)
@@ -231,12 +261,30 @@ def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_
             _check_state("h_final", h_final, B, D, a.device)
     plain = (dtype is torch.float32 and not reverse and h_init is None and not want_final
              and a.is_contiguous() and b.is_contiguous() and h.is_contiguous())
+    if workspace is not None and (not isinstance(workspace, torch.Tensor) or workspace.device != a.device
+                                  or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous CUDA tensor on a's device")
+    if workspace is None and stream is None and torch.cuda.is_current_stream_capturing():
+        need = workspace_bytes(a, b, h, h_init=h_init, h_final=h_final, reverse=reverse)
+        if need > 0:
+            # from the capture's memory pool; torch's allocations are 512-byte aligned
+            workspace = torch.zeros(need, dtype=torch.uint8, device=a.device)
     if index != torch.cuda.current_device():
         with torch.cuda.device(index):   # the library works on the current HIP device
-            _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index))
+            _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index), workspace)
     else:
-        _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index))
+        _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index), workspace)
     return (h, h_final) if want_final else h
+
+
+def workspace_bytes(a, b, h=None, *, h_init=None, h_final=None, reverse=False) -> int:
+    """Bytes of the lookback workspace a linrec_scan of these tensors may need on their device
+    (0: none); the size a ``workspace`` argument must have."""
+    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse)
+    out = ctypes.c_size_t(0)
+    with torch.cuda.device(a.get_device()):
+        _check(_lib.linrec_scan_ex_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return int(out.value)
 
 
 def linrec_scan_ex_raw(desc: linrec_scan_desc, stream_ptr: int = 0) -> int:

@@ -275,3 +275,31 @@ def test_default_plans_of_the_named_workloads(key):
     status, p = ex_plan(desc(B, L, D, dtype=dtype))
     assert status == binding.LINREC_OK
     assert (p["vec"], p["steps_per_lane"], p["waves"], p["lanes_per_row"], p["mode"]) == DEFAULT_PLANS[key]
+
+
+def test_workspace_sizes_without_a_device():
+    """The workspace-size entry points are host arithmetic (on a host without a GPU they assume a
+    256-CU part, like the plan entry points)."""
+    lib = binding.library()
+    for shape in ((8, 16384, 1024), (2, 262144, 64), (32, 4096, 256), (3, 100, 7), (1, 64, 8)):
+        need = lib.linrec_scan_workspace_bytes(*shape)
+        # the larger of the aligned and unaligned plans' needs
+        assert need == max(binding.linrec_scan_plan(*shape, aligned16=al)["workspace_bytes"] for al in (True, False))
+    assert binding.linrec_scan_plan(1, 64, 8)["workspace_bytes"] == 0   # one chunk: no carry to pass on
+    assert lib.linrec_scan_workspace_bytes(-1, 64, 8) == 0
+    d = desc(2, 262144, 64)
+    out = ctypes.c_size_t(7)
+    assert lib.linrec_scan_ex_workspace_bytes(ctypes.byref(d), ctypes.byref(out)) == binding.LINREC_OK
+    assert out.value == ex_plan(d)[1]["workspace_bytes"] > 0
+    assert lib.linrec_scan_ex_workspace_bytes(ctypes.byref(d), None) == binding.LINREC_ERR_INVALID_ARGUMENT
+    assert lib.linrec_scan_ex_workspace_bytes(None, ctypes.byref(out)) == binding.LINREC_ERR_INVALID_ARGUMENT
+
+
+def test_caller_workspace_entry_points_check_sizes_before_any_hip_call():
+    lib = binding.library()
+    assert lib.linrec_scan_ws(None, None, None, 0, 5, 5, None, 0, None) == binding.LINREC_OK
+    assert lib.linrec_scan_ws(None, None, None, -1, 5, 5, None, 0, None) == binding.LINREC_ERR_INVALID_ARGUMENT
+    d = desc(0, 10, 10)
+    d.a.ptr = d.b.ptr = d.h.ptr = None
+    assert lib.linrec_scan_ex_ws(ctypes.byref(d), None, 0, None) == binding.LINREC_OK
+    assert lib.linrec_scan_ex_ws(None, None, 0, None) == binding.LINREC_ERR_INVALID_ARGUMENT
