@@ -243,6 +243,32 @@ linrec_status linrec_scan_ws(const float *a, const float *b, float *h, int64_t B
 linrec_status linrec_scan_ex_ws(const linrec_scan_desc *desc, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
+/*
+ * linrec_scan_ex_noalloc -- linrec_scan_ex for callers that cannot allocate
+ * device memory at all: code under HIP graph capture (including the first
+ * call on a stream), tight serving loops, and harnesses that forbid
+ * hipMalloc.  It runs the same kernels as linrec_scan_ex with the same
+ * arguments, results, errors and environment, and calls no hipMalloc, hipFree
+ * or other allocating routine.
+ *
+ * Its lookback workspace is a static 16 MiB array in the library's device
+ * code, one per device, held from module load to process end.  A call whose
+ * plan needs more (linrec_scan_ex_workspace_bytes above 16 MiB, e.g. very
+ * long chains of small tiles) returns LINREC_ERR_INVALID_ARGUMENT and
+ * enqueues nothing; linrec_scan_ex_ws serves those.  Calls whose plan needs
+ * no workspace (a local carry, a single chunk) do not touch it.
+ *
+ * Every call on a device shares that device's array, and each call leaves it
+ * in the state the next one expects.  Calls that may overlap in time on one
+ * device (different streams, or graph replays concurrent with other calls)
+ * therefore race: order them on one stream.  The first call on a device
+ * enqueues a clear of the array (a fill kernel, no memset) on its stream
+ * before the scan.  If that call is being captured, the clear is recorded in
+ * the graph, so each replay clears the array first, and the next eager call
+ * clears it again.
+ */
+linrec_status linrec_scan_ex_noalloc(const linrec_scan_desc *desc, void *stream);
+
 /* Workspace bytes a linrec_scan_ws call of shape (B, L, D) may need on the
  * current device, whatever the buffers' alignment (0: none, or invalid
  * sizes).  Host arithmetic plus a query of the device's CU count. */

@@ -548,6 +548,50 @@ linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, voi
     return LINREC_OK;
 }
 
+// ----------------------------------------------------------------------------- static scratch
+
+// The lookback workspace of linrec_scan_ex_noalloc: a file-scope device array,
+// so that entry point never allocates.  Each device the library runs on holds
+// its own copy from module load to process end.  In host code `scratch` only
+// names the symbol: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchState {
+    void* ptr = nullptr;   // device address of `scratch` on this device
+    bool cleared = false;  // an eager clear has been enqueued
+    uint64_t calls = 0;
+};
+std::map<int, ScratchState> g_scratch;   // per device, under g_mutex
+
+// The device address of this device's scratch, cleared before its first use:
+// the clear is a fill kernel on the call's stream.  When that call is being
+// captured the clear is recorded in the graph (each replay then starts from a
+// clean scratch) and the next eager call clears it again.
+linrec_status scratch_for(int device, hipStream_t stream, void*& out) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    ScratchState& st = g_scratch[device];
+    if (st.ptr == nullptr) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(LINREC_ERR_HIP, "hipGetSymbolAddress(scratch): " + hip_text(e));
+        }
+        st.ptr = p;
+    }
+    st.calls += 1;
+    const bool eager = !capturing(stream);
+    if (!st.cleared || st.calls % kClearPeriod == 0) {
+        const linrec_status s = zero_fill(st.ptr, kScratchBytes, stream);
+        if (s != LINREC_OK) return s;
+        if (eager) st.cleared = true;
+    }
+    out = st.ptr;
+    return LINREC_OK;
+}
+
 // A caller's workspace: counted for the periodic clear, which this call then
 // enqueues on `stream` (never allocated or freed here).
 linrec_status use_caller_workspace(int device, void* ptr, size_t bytes, hipStream_t stream) {
@@ -598,6 +642,7 @@ struct WorkspaceSource {
     bool caller = false;   // true: the caller's (ptr, bytes), possibly null; false: the library's own
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool scratch = false;  // true: the device's static scratch (linrec_scan_ex_noalloc)
 };
 
 linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& src = WorkspaceSource{}) {
@@ -663,7 +708,14 @@ linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& s
     }
     void* ws = nullptr;
     if (p.workspace_bytes > 0 && p.geom.local_seqs == 0) {
-        if (src.caller) {
+        if (src.scratch) {
+            if (p.workspace_bytes > kScratchBytes)
+                return fail(LINREC_ERR_INVALID_ARGUMENT,
+                            "this call needs " + std::to_string(p.workspace_bytes) +
+                                " bytes of lookback workspace and the static scratch of linrec_scan_ex_noalloc "
+                                "holds " + std::to_string(kScratchBytes) + "; pass a workspace to linrec_scan_ex_ws");
+            if ((s = scratch_for(device, hs, ws)) != LINREC_OK) return s;
+        } else if (src.caller) {
             if (src.ptr == nullptr || src.bytes < p.workspace_bytes)
                 return fail(LINREC_ERR_INVALID_ARGUMENT,
                             "this call needs a workspace of " + std::to_string(p.workspace_bytes) + " bytes, got " +
@@ -816,6 +868,16 @@ linrec_status linrec_scan_ex_ws(const linrec_scan_desc* desc, void* workspace, s
     const linrec_status s = make_problem(desc, pr);
     if (s != LINREC_OK) return s;
     return run_scan(pr, stream, WorkspaceSource{true, workspace, workspace_bytes});
+}
+
+linrec_status linrec_scan_ex_noalloc(const linrec_scan_desc* desc, void* stream) {
+    t_last_error.clear();
+    Problem pr;
+    const linrec_status s = make_problem(desc, pr);
+    if (s != LINREC_OK) return s;
+    WorkspaceSource src;
+    src.scratch = true;
+    return run_scan(pr, stream, src);
 }
 
 linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, int64_t L, int64_t D, void* stream) {

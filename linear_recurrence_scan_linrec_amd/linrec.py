@@ -39,6 +39,7 @@ EXPORTED = (
     "linrec_scan_ex_ws",
     "linrec_scan_workspace_bytes",
     "linrec_scan_ex_workspace_bytes",
+    "linrec_scan_ex_noalloc",
 )
 
 
@@ -121,6 +122,8 @@ def _load() -> ctypes.CDLL:
     lib.linrec_scan_workspace_bytes.argtypes = [i64, i64, i64]
     lib.linrec_scan_ex_workspace_bytes.restype = ctypes.c_int
     lib.linrec_scan_ex_workspace_bytes.argtypes = [ctypes.POINTER(linrec_scan_desc), ctypes.POINTER(ctypes.c_size_t)]
+    lib.linrec_scan_ex_noalloc.restype = ctypes.c_int
+    lib.linrec_scan_ex_noalloc.argtypes = [ctypes.POINTER(linrec_scan_desc), vp]
     return lib
 
 
