@@ -210,18 +210,30 @@ def test_resets_give_b_exactly(lr):
     assert np.array_equal(h[mask], b[mask])
 
 
-def test_run_to_run(lr):
-    """Two runs agree within the bar; the chained tiles may pick different bracketings."""
-    for name in ("pages_shape", "long_sequence"):
-        a_np, b_np = li.workload_inputs(name)
-        a = torch.from_numpy(a_np).cuda()
-        b = torch.from_numpy(b_np).cuda()
-        h1 = lr.linrec_scan(a, b)
-        h2 = lr.linrec_scan(a, b)
-        torch.cuda.synchronize()
-        diff = ((h1 - h2).abs() / (1 + h1.abs())).max().item()
-        say(f"[determinism] {name}: max run-to-run ratio {diff:.3e}, bitwise equal {torch.equal(h1, h2)}")
-        assert diff <= TOL
+# Workloads whose default plan keeps the carry local (persistent workgroups that own whole
+# sequences): every output then has one fixed evaluation order.  The one-tile plan of
+# long_sequence looks back, and which predecessor has published its inclusive state when a tile
+# reads it depends on timing, so its bracketing may differ from run to run.
+LOCAL_CARRY_WORKLOADS = ("pages_shape", "wide_channels", "near_unit_resets")
+
+
+@pytest.mark.parametrize("name", LOCAL_CARRY_WORKLOADS + ("long_sequence",))
+def test_run_to_run(lr, name):
+    """Local-carry plans are bitwise equal from run to run; lookback plans agree within the bar."""
+    a_np, b_np = li.workload_inputs(name)
+    a = torch.from_numpy(a_np).cuda()
+    b = torch.from_numpy(b_np).cuda()
+    del a_np, b_np
+    h1 = lr.linrec_scan(a, b)
+    h2 = lr.linrec_scan(a, b)
+    h3 = lr.linrec_scan(a, b)
+    torch.cuda.synchronize()
+    diff = max(((h1 - h).abs() / (1 + h1.abs())).max().item() for h in (h2, h3))
+    equal = torch.equal(h1, h2) and torch.equal(h1, h3)
+    say(f"[determinism] {name}: max run-to-run ratio {diff:.3e}, bitwise equal {equal}")
+    if name in LOCAL_CARRY_WORKLOADS:
+        assert equal, f"{name}: local-carry plan not bitwise reproducible (max ratio {diff:.3e})"
+    assert diff <= TOL
 
 
 def test_non_default_stream(lr):
