@@ -130,6 +130,8 @@ def parse_args():
     p.add_argument("--cold", type=int, default=0, metavar="N",
                    help="after the timed steps, N launches each preceded by a cache-evicting write (untimed)")
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
+    p.add_argument("--ceiling-shape", metavar="R,U,G",
+                   help="run the ceiling only in this walk (rows R), unroll U and groups per CU G (for counter runs)")
     p.add_argument("--regions", type=int, default=10,
                    help="further regions of 10 launches whose means give median/p10/p90 (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,21 +289,25 @@ def region_mean_us(torch, launch, count: int, stream, first: int = 0) -> float:
     return s_ev.elapsed_time(e_ev) * 1e3 / count
 
 
-def measure_ceiling(torch, xs, ys, zs, rows: int, stream, warmup=3, reps=10):
+def measure_ceiling(torch, xs, ys, zs, rows: int, stream, warmup=3, reps=10, only=None):
     """Best mean launch time (us) of the read-2-write-1 stream over the given buffers (any storage,
-    reinterpreted as float32) for each walk order; returns {order: {...}}."""
+    reinterpreted as float32) for each walk order; returns {order: {...}}.  ``only`` = (R, U, G)
+    restricts the sweep to one walk and launch shape."""
     from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
 
     flat = lambda t: t.reshape(-1).view(torch.float32)  # noqa: E731
     X, Y, Z = [flat(t) for t in xs], [flat(t) for t in ys], [flat(t) for t in zs]
     n = X[0].numel()
     out = {}
-    for order, r in (("contiguous", 1), ("scan_order", rows)):
+    orders = (("contiguous", 1), ("scan_order", rows))
+    if only is not None:
+        orders = (("contiguous" if only[0] == 1 else "scan_order", only[0]),)
+    for order, r in orders:
         best = None
-        for unroll in (1, 2, 4):
+        for unroll in ((1, 2, 4) if only is None else (only[1],)):
             if n % (r * 256 * unroll) != 0:
                 continue
-            for gpc in (1, 2, 4, 8):
+            for gpc in ((1, 2, 4, 8) if only is None else (only[2],)):
                 def launch(k, r=r, unroll=unroll, gpc=gpc):
                     sc.stream_r2w1(X[k % len(X)], Y[k % len(X)], Z[k % len(X)], r, unroll, gpc, stream)
                 for k in range(warmup):
@@ -441,7 +447,8 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_ceiling:
-        ceil = measure_ceiling(torch, a_sets, b_sets, h_sets, w.B, stream)
+        only = tuple(int(x) for x in args.ceiling_shape.split(",")) if args.ceiling_shape else None
+        ceil = measure_ceiling(torch, a_sets, b_sets, h_sets, w.B, stream, only=only)
         for v in ceil.values():
             v["gbs"] = round(3 * elem * n / (v["us"] * 1e-6) / 1e9, 1)
         out["ceiling"] = dict(ceil, kind="read-2-write-1 stream z = x + y (libstream_ceiling.so) over the same "
