@@ -158,3 +158,39 @@ def test_capture_without_warm_up(lr):
         h_w = lr.linrec_scan(a, b, workspace=ws)
         torch.cuda.synchronize()
         assert worst_ratio(h_e, ref) <= TOL and worst_ratio(h_w, ref) <= TOL
+
+
+def test_epoch_bookkeeping_across_grids_of_every_size(lr):
+    """Thirty lookback calls in a row on one stream and one workspace, with grids from 1 to
+    thousands of workgroups (one-tile and persistent plans, fewer and more workgroups than slot
+    lines).  Each call counts its workgroups into slot lines that depend on its grid, and the last
+    one advances the epoch; a count left over, or an epoch advanced early, would let a later call
+    accept stale status words.  Every output must match the oracle."""
+    import os
+    old = os.environ.get("LINREC_TILE")
+    rng = np.random.default_rng(2400)
+    # (shape, tile override): grids of 1, 2, 5, 37, 255, 256, 257 and ~2000+ workgroups
+    cases = [((1, 3000, 64), "m=1,t=4,w=1,p=16"), ((2, 9000, 64), "m=0,t=4,w=8,p=32,l=0,q=1"),
+             ((1, 700, 8), "m=1,t=4,w=1,p=2"), ((3, 20000, 24), ""), ((2, 40000, 64), ""),
+             ((32, 2048, 256), "m=0,t=4,w=8,p=32,l=0"), ((5, 12000, 136), "m=0,t=8,w=2,p=8,l=0,q=2"),
+             ((4, 30000, 64), "m=1,t=8,w=7,p=8")]
+    try:
+        for k in range(30):
+            shape, tile = cases[int(rng.integers(len(cases)))]
+            if tile:
+                os.environ["LINREC_TILE"] = tile
+            else:
+                os.environ.pop("LINREC_TILE", None)
+            plan = lr.linrec_scan_plan(*shape)
+            a_np, b_np = li.make_inputs(*shape, seed=2400 + k, a_lo=0.9, a_hi=1.0)
+            h = lr.linrec_scan(torch.from_numpy(a_np).cuda(), torch.from_numpy(b_np).cuda())
+            torch.cuda.synchronize()
+            worst = worst_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
+            say(f"[epochs] call {k}: {shape} {tile or 'default'} tiles={plan['tiles']}: {worst:.2e}")
+            assert worst <= TOL, (k, shape, tile, worst)
+        assert lr.linrec_device_timeouts() == 0
+    finally:
+        if old is None:
+            os.environ.pop("LINREC_TILE", None)
+        else:
+            os.environ["LINREC_TILE"] = old
