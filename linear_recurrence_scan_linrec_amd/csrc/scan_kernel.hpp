@@ -497,13 +497,26 @@ __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* 
 
 // Status arrays of a lookback workspace, nstatus words each: the tile pair
 // (its product of decays as the fp32 pair hi + lo, which keeps about 48 bits
-// of it, and B), and the inclusive state after the tile.
+// of it, or hi alone for 16-bit storage; and B), and the inclusive state
+// after the tile.
 struct StatusArrays {
     uint64_t *a_hi, *a_lo, *b, *p;
 };
 
 __device__ __forceinline__ StatusArrays status_arrays(uint64_t* stat, int64_t nstatus) {
     return StatusArrays{stat, stat + nstatus, stat + 2 * nstatus, stat + 3 * nstatus};
+}
+
+// With 16-bit storage the published product of decays is the single fp32 word
+// hi (a_lo is neither written nor read).  Rounding it once per tile costs at
+// most 2^-24 of the product; with a constant decay those errors repeat, and
+// they add up over the chain's memory of about 1 / (1 - tile product) tiles,
+// which at a decay of 0.99999 and 448 positions per tile is 224 tiles: about
+// 1.3e-5 of the state, against outputs rounded at 2^-8 (bf16) or 2^-11 (fp16).
+// fp32 outputs keep the hi + lo pair.
+template <typename S>
+constexpr bool product_in_one_word() {
+    return sizeof(S) == 2;
 }
 
 // Decoupled lookback for one channel of a tile in chunk `chunk` (> 0): reads
@@ -536,7 +549,7 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
                 const int64_t k = idx - (chunk - (j - m)) * stride;
                 wp[m] = observe(st.p + k);
                 wh[m] = observe(st.a_hi + k);
-                wl[m] = observe(st.a_lo + k);
+                if constexpr (!product_in_one_word<S>()) wl[m] = observe(st.a_lo + k);
                 wb[m] = observe(st.b + k);
             }
         }
@@ -549,8 +562,11 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
             if (tag_of(wp[m]) == tag_inc) {
                 h_prev = payload_of(wp[m]);
                 found = true;
-            } else if (tag_of(wh[m]) == tag_agg && tag_of(wl[m]) == tag_agg && tag_of(wb[m]) == tag_agg) {
-                const double pa = static_cast<double>(payload_of(wh[m])) + static_cast<double>(payload_of(wl[m]));
+            } else if (tag_of(wh[m]) == tag_agg && (product_in_one_word<S>() || tag_of(wl[m]) == tag_agg) &&
+                       tag_of(wb[m]) == tag_agg) {
+                const double pa = product_in_one_word<S>()
+                                      ? static_cast<double>(payload_of(wh[m]))
+                                      : static_cast<double>(payload_of(wh[m])) + static_cast<double>(payload_of(wl[m]));
                 acc_b = __builtin_fma(acc_a, static_cast<double>(payload_of(wb[m])), acc_b);
                 acc_a = acc_a * pa;
                 folded = m + 1;
@@ -817,7 +833,8 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                 if (has_successor) {
                     const float hi = static_cast<float>(ta);
                     publish(st.a_hi + idx, tag_agg, hi);
-                    publish(st.a_lo + idx, tag_agg, static_cast<float>(ta - static_cast<double>(hi)));
+                    if constexpr (!product_in_one_word<S>())
+                        publish(st.a_lo + idx, tag_agg, static_cast<float>(ta - static_cast<double>(hi)));
                     publish(st.b + idx, tag_agg, static_cast<float>(tb));
                 }
                 h_in = g.lookback_window > 2

@@ -186,6 +186,35 @@ def test_constant_decay_near_one(lr, decay, tile_env):
             check(h, ref, torch.float32, f"constant decay {decay} {name} {tile or 'default'}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
+def test_half_storage_constant_decay_long_chain(lr, dtype, tile_env):
+    """16-bit storage publishes each tile's product of decays as one fp32 word, rounded once per
+    tile; with a constant decay those roundings repeat along the chain.  Over 586 chunks per
+    sequence at (2, 262144, 64), with the closest decay below 1 that the storage type holds
+    (1 - 2^-8 for bf16, 1 - 2^-11 for fp16), time-broadcast and materialised, one tile per
+    workgroup and persistent lookback: every output within the storage type's bar.
+
+    A decay of exactly 1 is left out at this length: rounding errors made while |h| is in the
+    hundreds then never fade, and a plain sequential fp32 loop misses the bar by 4x (bf16
+    outputs), 11x (fp16) and 85x (fp32) where the running sum comes back near zero."""
+    B, L, D = 2, 262144, 64
+    decay = 1.0 - 2.0 ** (-8 if dtype == torch.bfloat16 else -11)
+    _, b32 = li.make_inputs(B, L, D, seed=330)
+    b = torch.from_numpy(b32).cuda().to(dtype)
+    b_np = b.float().cpu().numpy()
+    a_np = np.full((B, L, D), decay, dtype=np.float32)
+    ref = oracle.linrec_oracle_f64(a_np, b_np)
+    say(f"[ex] {dtype} constant decay {decay}: max |h| = {np.abs(ref).max():.1f}")
+    a_full = torch.from_numpy(a_np).cuda().to(dtype)
+    a_bcast = torch.full((1, 1, D), decay, dtype=dtype, device="cuda").expand(B, L, D)
+    for tile in ("", "m=0,t=8,w=8,p=16,l=0"):
+        set_tile(tile)
+        for name, a in (("materialised", a_full), ("time-broadcast", a_bcast)):
+            h = lr.linrec_scan(a, b)
+            torch.cuda.synchronize()
+            check(h, ref, dtype, f"{dtype} constant decay {decay} {name} {tile or 'default'}")
+
+
 # ----------------------------------------------------------------------------- 16-bit storage
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16], ids=["bf16", "f16"])
