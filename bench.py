@@ -53,6 +53,7 @@ METRIC = "achieved HBM GB/s and % of peak, linrec_scan B=32 L=4096 D=256 fp32"
 # unchanged keep a counter measurement valid
 KERNEL_SOURCES = [
     ROOT / "linear_recurrence_scan_linrec_amd" / "csrc" / "scan_kernel.hpp",
+    ROOT / "linear_recurrence_scan_linrec_amd" / "csrc" / "call_epoch.hpp",
 ]
 PROFILES = ROOT / "profiles"
 

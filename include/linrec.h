@@ -62,7 +62,8 @@ typedef enum linrec_status {
  * Workspace: when L spans several tiles and the tiles must look back across
  * workgroups, the call uses a workspace of status words.  The library keeps
  * one per (device, stream): it allocates it on the first call on that stream
- * that needs one (hipMalloc and a clear, outside any stream), replaces it with
+ * that needs one (hipMalloc, then a clear enqueued on that stream before the
+ * scan), replaces it with
  * a larger one when a shape needs more, and frees all of them in
  * linrec_release().  A replaced workspace is kept, not freed, until then (a
  * graph captured with it may still be replayed).  Calls on one stream are

@@ -531,10 +531,14 @@ linrec_status acquire_workspace(int device, size_t need, hipStream_t stream, voi
             (void)hipGetLastError();
             return fail(LINREC_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(bytes) + " workspace bytes: " + hip_text(e));
         }
-        e = hipMemset(p, 0, bytes);
-        if (e != hipSuccess) {
+        // cleared on the call's stream, so the clear is ordered before the
+        // scan: a hipMemset would run on the null stream, which work on a
+        // non-blocking stream (torch's side streams) does not wait for, and
+        // the first scan could then read uncleared slot lines
+        const linrec_status cleared = zero_fill(p, bytes, stream);
+        if (cleared != LINREC_OK) {
             (void)hipFree(p);
-            return fail(LINREC_ERR_HIP, "clearing the new workspace: " + hip_text(e));
+            return cleared;
         }
         if (ws.ptr != nullptr) g_retired.emplace_back(device, ws.ptr);
         ws = Workspace{p, bytes, 0};

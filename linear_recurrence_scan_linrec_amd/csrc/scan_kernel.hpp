@@ -57,19 +57,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "call_epoch.hpp"
+
 namespace linrec {
 
 constexpr int kWave = 64;
 constexpr uint32_t kKindAggregate = 1u;   // payload: one component of the tile pair
 constexpr uint32_t kKindInclusive = 2u;   // payload: state after the tile's last position
 
-// Workspace: a header, kDoneSlots slot lines (128 bytes each: word 0 counts
-// the workgroups of the current call that hold the epoch, word 1 is the epoch
-// of the current call), then kStatusArrays status arrays of nstatus words
-// (see StatusArrays).
+// Workspace: a header, the kDoneSlots slot lines of the call epoch
+// (call_epoch.hpp), then kStatusArrays status arrays of nstatus words (see
+// StatusArrays).
 constexpr int kMaxLocalSeqs = 4;  // sequences one workgroup may carry locally
-constexpr int kLineWords = 32;    // uint32 words per 128-byte line
-constexpr int kDoneSlots = 256;
 constexpr int kStatusArrays = 4;
 
 struct WorkspaceHeader {
@@ -597,64 +596,42 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
 }
 
 // ---------------------------------------------------------------------------
-// Call epochs.  Workgroup k of a call belongs to slot line k * kDoneSlots / grid
-// (contiguous ranges, so slots fill one after another during the call rather
-// than all at its end).  Each workgroup reads the epoch from its slot line and
-// then adds one to the line's count; the workgroup that fills a line adds one
-// to `finished`, and the one that fills that writes the next epoch into every
-// slot line.  By then every workgroup of the call holds its epoch, and the
-// next call on the stream cannot start before this one has ended, so the order
-// in which workgroups run does not matter.  Spreading reads and counts over
-// many lines keeps same-address traffic rare.
+// Call epochs (call_epoch.hpp) over agent-scope atomics.  The slot lines
+// follow the header; every wave of a workgroup that publishes or reads status
+// words reads the epoch before the workgroup's count_done (behind a barrier).
 
-__device__ __forceinline__ uint32_t* slot_line(WorkspaceHeader* hdr, int64_t slot) {
-    return reinterpret_cast<uint32_t*>(hdr + 1) + slot * kLineWords;
-}
+struct AgentAtomics {
+    __device__ static uint32_t load(uint32_t* p) { return observe32(p); }
+    __device__ static uint32_t add(uint32_t* p, uint32_t v) {
+        return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static void store(uint32_t* p, uint32_t v) {
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+};
 
-__device__ __forceinline__ int64_t slot_of(int64_t group, int64_t groups) { return group * kDoneSlots / groups; }
-
-// first workgroup of slot `slot` (ceil(slot * groups / kDoneSlots))
-__device__ __forceinline__ int64_t slot_begin(int64_t slot, int64_t groups) {
-    return (slot * groups + kDoneSlots - 1) / kDoneSlots;
+__device__ __forceinline__ EpochWords epoch_words(WorkspaceHeader* hdr) {
+    return EpochWords{reinterpret_cast<uint32_t*>(hdr + 1), &hdr->finished};
 }
 
 __device__ __forceinline__ uint32_t call_epoch(WorkspaceHeader* hdr) {
-    return observe32(slot_line(hdr, slot_of(blockIdx.x, gridDim.x)) + 1);
+    return epoch_of_call<AgentAtomics>(epoch_words(hdr), blockIdx.x, gridDim.x);
 }
 
-// Lane 0 counts the workgroup in its slot line.  The addend is computed from
-// the epoch this workgroup read (epochs are below 2^30, so it is 1): the count
-// cannot be performed before that read has returned.  Returns the count
-// before the addition on lane 0, 0 elsewhere.
+// Lane 0 counts the workgroup in its slot line; returns the count before the
+// addition on lane 0, 0 elsewhere.
 __device__ __forceinline__ uint32_t count_in(WorkspaceHeader* hdr, uint32_t epoch, int lane) {
     if (lane != 0) return 0u;
-    return __hip_atomic_fetch_add(slot_line(hdr, slot_of(blockIdx.x, gridDim.x)), 1u + (epoch >> 30),
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return epoch_count_in<AgentAtomics>(epoch_words(hdr), blockIdx.x, gridDim.x, epoch);
 }
 
-// Whole wave: given count_in's result, rearm the slot line if this workgroup
-// filled it, and advance the epoch if it filled the last line.
+// Whole wave, after a barrier that every wave reading the epoch has passed:
+// given count_in's result, rearm the slot line if this workgroup filled it,
+// and advance the epoch if it filled the last line.
 __device__ inline void count_done(WorkspaceHeader* hdr, uint32_t epoch, uint32_t before, int lane) {
-    const int64_t groups = gridDim.x;
-    const int64_t slot = slot_of(blockIdx.x, groups);
-    int last = 0;
-    if (lane == 0) {
-        const uint32_t expect = static_cast<uint32_t>(slot_begin(slot + 1, groups) - slot_begin(slot, groups));
-        if (before + 1 == expect) {
-            __hip_atomic_store(slot_line(hdr, slot), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t lines = static_cast<uint32_t>(groups < kDoneSlots ? groups : kDoneSlots);
-            const uint32_t f = __hip_atomic_fetch_add(&hdr->finished, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (f + 1 == lines) {
-                __hip_atomic_store(&hdr->finished, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                last = 1;
-            }
-        }
-    }
-    if (__shfl(last, 0) != 0) {
-        const uint32_t next = (epoch + 1u) & 0x3fffffffu;
-        for (int k = lane; k < kDoneSlots; k += kWave)
-            __hip_atomic_store(slot_line(hdr, k) + 1, next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const EpochWords w = epoch_words(hdr);
+    const int last = lane == 0 && epoch_count_done<AgentAtomics>(w, blockIdx.x, gridDim.x, before) ? 1 : 0;
+    if (__shfl(last, 0) != 0) epoch_advance<AgentAtomics>(w, epoch, lane, kWave);
 }
 
 // LDS shared by the waves of one workgroup.  Between the two barriers of a
@@ -911,10 +888,10 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         __shared__ LocalCarry<VEC> local;
         const int carry = wave - W;
         const int c = carry * kWave + lane;
-        uint32_t epoch = 0;
+        uint32_t epoch = 0, before = 0;
         if (chained) {
             epoch = call_epoch(hdr);
-            if (carry == 0) count_done(hdr, epoch, count_in(hdr, epoch, lane), lane);
+            if (carry == 0) before = count_in(hdr, epoch, lane);
         }
         bool recomputed = false;
         int slot = 0;   // sequence slot of the local carry: tiles cycle through local_seqs sequences
@@ -924,8 +901,13 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
             if (g.local_seqs > 0 && ++slot == g.local_seqs) slot = 0;
             __syncthreads();   // the states entering the waves are in LDS
         }
-        if (chained && __ballot(recomputed) != 0 && lane == 0)
+        if (!chained) return;
+        if (__ballot(recomputed) != 0 && lane == 0)
             __hip_atomic_fetch_add(&hdr->timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // after the tile loop's barriers, which every carry wave (each reads
+        // the epoch) has passed; a workgroup without tiles passes none, but
+        // then its carry waves touch no status word
+        if (carry == 0) count_done(hdr, epoch, before, lane);
         return;
     }
 

@@ -78,7 +78,31 @@ def test_two_streams_run_lookback_scans_concurrently(lr, own):
         for k, (a_np, b_np, _, _, h) in enumerate(work[s]):
             worst = worst_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
             assert worst <= TOL, (s, k, worst)
-    say("[streams] all 16 outputs within the bar")
+    say(f"[streams] all 16 outputs within the bar; recomputed waits on the device: {lr.linrec_device_timeouts()}")
+
+
+def test_fresh_workspaces_are_cleared_before_their_first_scan(lr):
+    """The first lookback call on a stream allocates that stream's workspace and must clear it
+    before its scan reads the slot lines.  Each round releases every workspace (so new ones may
+    reuse memory that held an earlier workspace's lines and status words), then enqueues the first
+    scan on each of three side streams at once, with no synchronisation.  torch's side streams do
+    not wait for the null stream, so a clear issued there could still be running when the scan
+    reads the lines; the library clears on the call's own stream.  Every output must match the
+    oracle with no predecessor recomputed (a scan that read uncleared lines would see mixed
+    epochs and fall back to recomputing)."""
+    work = cases(3, LOOKBACK_SHAPE, 2600)
+    refs = [oracle.linrec_oracle_f64(a_np, b_np) for a_np, b_np, *_ in work]
+    for r in range(4):
+        torch.cuda.synchronize()
+        lr.linrec_release()
+        streams = [torch.cuda.Stream() for _ in work]
+        for (_, _, a, b, h), stream in zip(work, streams):
+            lr.linrec_scan(a, b, h, stream=stream)
+        torch.cuda.synchronize()
+        waits = lr.linrec_device_timeouts()
+        worst = max(worst_ratio(h, ref) for (*_, h), ref in zip(work, refs))
+        say(f"[fresh] round {r}: worst {worst:.2e}, recomputed waits {waits}")
+        assert worst <= TOL and waits == 0, (r, worst, waits)
 
 
 def test_caller_workspace_argument_checks(lr):
@@ -158,6 +182,7 @@ def test_capture_without_warm_up(lr):
         h_w = lr.linrec_scan(a, b, workspace=ws)
         torch.cuda.synchronize()
         assert worst_ratio(h_e, ref) <= TOL and worst_ratio(h_w, ref) <= TOL
+        say(f"[capture] recomputed waits in the library's workspaces: {lr.linrec_device_timeouts()}")
 
 
 def test_epoch_bookkeeping_across_grids_of_every_size(lr):
@@ -165,9 +190,12 @@ def test_epoch_bookkeeping_across_grids_of_every_size(lr):
     thousands of workgroups (one-tile and persistent plans, fewer and more workgroups than slot
     lines).  Each call counts its workgroups into slot lines that depend on its grid, and the last
     one advances the epoch; a count left over, or an epoch advanced early, would let a later call
-    accept stale status words.  Every output must match the oracle."""
+    accept stale status words.  Every output must match the oracle, and no call may fall back to
+    recomputing a predecessor (a call that read another call's epoch would have to)."""
     import os
     old = os.environ.get("LINREC_TILE")
+    say(f"[epochs] recomputed waits before the release: {lr.linrec_device_timeouts()}")
+    lr.linrec_release()                  # the count of recomputed waits runs from here
     rng = np.random.default_rng(2400)
     # (shape, tile override): grids of 1, 2, 5, 37, 255, 256, 257 and ~2000+ workgroups
     cases = [((1, 3000, 64), "m=1,t=4,w=1,p=16"), ((2, 9000, 64), "m=0,t=4,w=8,p=32,l=0,q=1"),
@@ -186,9 +214,11 @@ def test_epoch_bookkeeping_across_grids_of_every_size(lr):
             h = lr.linrec_scan(torch.from_numpy(a_np).cuda(), torch.from_numpy(b_np).cuda())
             torch.cuda.synchronize()
             worst = worst_ratio(h, oracle.linrec_oracle_f64(a_np, b_np))
-            say(f"[epochs] call {k}: {shape} {tile or 'default'} tiles={plan['tiles']}: {worst:.2e}")
+            waits = lr.linrec_device_timeouts()
+            say(f"[epochs] call {k}: {shape} {tile or 'default'} tiles={plan['tiles']}: {worst:.2e}, "
+                f"recomputed waits so far {waits}")
             assert worst <= TOL, (k, shape, tile, worst)
-        assert lr.linrec_device_timeouts() == 0
+            assert waits == 0, (k, shape, tile, waits)
     finally:
         if old is None:
             os.environ.pop("LINREC_TILE", None)
