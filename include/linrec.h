@@ -63,9 +63,8 @@ typedef enum linrec_status {
  * workgroups, the call uses a workspace of status words.  The library keeps
  * one per (device, stream): it allocates it on the first call on that stream
  * that needs one (hipMalloc, then a clear enqueued on that stream before the
- * scan), replaces it with
- * a larger one when a shape needs more, and frees all of them in
- * linrec_release().  A replaced workspace is kept, not freed, until then (a
+ * scan), replaces it with a larger one when a shape needs more, and frees all
+ * of them in linrec_release().  A replaced workspace is kept, not freed, until then (a
  * graph captured with it may still be replayed).  Calls on one stream are
  * ordered, and calls on different streams use different workspaces, so
  * concurrent streams never share status words.  Each stream that makes such
@@ -226,7 +225,11 @@ linrec_status linrec_scan_ex_plan(const linrec_scan_desc *desc, linrec_plan *pla
  *   workspace        device memory of the current device, 256-byte aligned,
  *                    at least the bytes the *_workspace_bytes functions give,
  *                    overlapping no operand, and ZERO-FILLED before its first
- *                    use (e.g. hipMemset).  The library keeps it consistent
+ *                    use, the clear ordered before that call (e.g.
+ *                    hipMemsetAsync on the call's stream, or a hipMemset
+ *                    followed by hipDeviceSynchronize: a plain hipMemset runs
+ *                    on the null stream, which non-blocking streams do not
+ *                    wait for).  The library keeps it consistent
  *                    from call to call afterwards (every 2^29 calls on one
  *                    workspace, a call also enqueues a clear of it on its
  *                    stream).  It may serve calls of any shape.
