@@ -162,17 +162,25 @@ typedef struct linrec_operand {
  *   reverse   0: the recurrence runs forward in t, as in linrec_scan.
  *             1: it runs backward: h[i,L-1,d] = b[i,L-1,d] and
  *                h[i,t,d] = a[i,t,d] * h[i,t+1,d] + b[i,t,d] for t = L-2 .. 0
- *                (the time reversal of the recurrence; over an incoming
- *                gradient g with a shifted one step, a'[t] = a[t+1], it gives
- *                dLoss/db of a forward scan).  Not on the pages that define
- *                the forward recurrence.
+ *                (the time reversal of the recurrence).
+ *             2: it runs backward with each decay taken one time step ahead:
+ *                h[i,L-1,d] = b[i,L-1,d] (plus h_init[i,d], with decay 1) and
+ *                h[i,t,d] = a[i,t+1,d] * h[i,t+1,d] + b[i,t,d].  Over an
+ *                incoming gradient g as b, this is dLoss/db of the forward
+ *                scan over the same a, read without a shifted copy of a;
+ *                dLoss/da[t] is then dLoss/db[t] * h[t-1] of the forward scan.
+ *                A sequence taken in pieces chains through
+ *                h_init = a[:, L] * (the next piece's result at its first
+ *                step).  a[i,0,d] is never read.
+ *             The backward forms are not on the pages that define the forward
+ *             recurrence.
  *   a, b, h   operands; h.ptr is written (cast away its const).  h's rows
  *             (i, t) must not overlap one another, and h must not overlap a
  *             or b (a and b may overlap each other).
  *   h_init    NULL, or a (B, D) row-major fp32 device buffer: the state before
  *             the first step of the scan order, so that the first step is
  *             h = a * h_init + b instead of h = b (forward: t = 0; reverse:
- *             t = L-1).  This generalises the running carry between chunks
+ *             t = L-1; with reverse = 2 the decay of that step is 1).  This generalises the running carry between chunks
  *             of the pages' kernels (the running-carry passage of the first
  *             reasoning block of the Kimi-K2.6 l1_p9 transcript) to a carry
  *             between calls.

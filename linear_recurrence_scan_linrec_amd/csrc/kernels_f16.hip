@@ -3,6 +3,6 @@
 
 namespace linrec_host {
 
-const Launch* pick_launch_f16(const TileShape& s) { return pick_launch<linrec::F16>(s); }
+const Launch* pick_launch_f16(const TileShape& s, bool ahead) { return pick_launch<linrec::F16>(s, ahead); }
 
 }  // namespace linrec_host

@@ -3,6 +3,6 @@
 
 namespace linrec_host {
 
-const Launch* pick_launch_f32(const TileShape& s) { return pick_launch<float>(s); }
+const Launch* pick_launch_f32(const TileShape& s, bool ahead) { return pick_launch<float>(s, ahead); }
 
 }  // namespace linrec_host

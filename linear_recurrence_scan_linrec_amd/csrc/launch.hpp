@@ -55,8 +55,9 @@ struct Launch {
 };
 
 // Table lookups, one per storage type; nullptr when the shape has no instance.
-const Launch* pick_launch_f32(const TileShape& s);
-const Launch* pick_launch_bf16(const TileShape& s);
-const Launch* pick_launch_f16(const TileShape& s);
+// `ahead`: the reverse form with the decays one time step ahead.
+const Launch* pick_launch_f32(const TileShape& s, bool ahead);
+const Launch* pick_launch_bf16(const TileShape& s, bool ahead);
+const Launch* pick_launch_f16(const TileShape& s, bool ahead);
 
 }  // namespace linrec_host

@@ -253,7 +253,7 @@ linrec_status make_problem(const linrec_scan_desc* d, Problem& p) {
     if (q.B < 0 || q.L < 0 || q.D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
     if (q.dtype != LINREC_F32 && q.dtype != LINREC_BF16 && q.dtype != LINREC_F16)
         return fail(LINREC_ERR_INVALID_ARGUMENT, "dtype must be LINREC_F32, LINREC_BF16 or LINREC_F16");
-    if (q.reverse != 0 && q.reverse != 1) return fail(LINREC_ERR_INVALID_ARGUMENT, "reverse must be 0 or 1");
+    if (q.reverse < 0 || q.reverse > 2) return fail(LINREC_ERR_INVALID_ARGUMENT, "reverse must be 0, 1 or 2");
     linrec_operand* ops[3] = {&q.a, &q.b, &q.h};
     for (linrec_operand* o : ops)
         if (o->stride_b < 0 || o->stride_l < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "strides must be >= 0");
@@ -314,7 +314,7 @@ linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     g.h_sb = q.h.stride_b; g.h_sl = q.h.stride_l;
     g.h_init = q.h_init;
     g.h_final = q.h_final;
-    g.reverse = q.reverse;
+    g.reverse = q.reverse != 0 ? 1 : 0;   // 2: reverse, with the decays one time step ahead
     g.spin_limit = spin_limit();
     if (q.B == 0 || q.L == 0 || q.D == 0) {
         p.tiles = 0;
@@ -412,11 +412,11 @@ int64_t local_grid(Plan& p, int64_t resident, int cus) {
     return 0;
 }
 
-const Launch* pick_launch(int32_t dtype, const TileShape& s) {
+const Launch* pick_launch(int32_t dtype, const TileShape& s, bool ahead) {
     switch (dtype) {
-        case LINREC_F32: return linrec_host::pick_launch_f32(s);
-        case LINREC_BF16: return linrec_host::pick_launch_bf16(s);
-        case LINREC_F16: return linrec_host::pick_launch_f16(s);
+        case LINREC_F32: return linrec_host::pick_launch_f32(s, ahead);
+        case LINREC_BF16: return linrec_host::pick_launch_bf16(s, ahead);
+        case LINREC_F16: return linrec_host::pick_launch_f16(s, ahead);
         default: return nullptr;
     }
 }
@@ -693,7 +693,8 @@ linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& s
         return LINREC_OK;
     }
 
-    const Launch* fn = pick_launch(q.dtype, p.tile);
+    const bool ahead = q.reverse == 2;   // the reverse form with the decays one time step ahead
+    const Launch* fn = pick_launch(q.dtype, p.tile, ahead);
     if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
     const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
     int64_t groups = p.tiles;   // one tile per workgroup
@@ -743,8 +744,13 @@ linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& s
     uint64_t* stat = ws ? reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + sizeof(WorkspaceHeader) +
                                                       linrec::kDoneBytes)
                         : nullptr;
+    // decays one time step ahead: the kernel reads a through a pointer
+    // advanced by one time step, and never reads that pointer's row L-1,
+    // which would be a's row L (load_tile)
+    const void* a_arg =
+        ahead ? static_cast<const void*>(static_cast<const char*>(q.a.ptr) + q.a.stride_l * pr.es) : q.a.ptr;
     (void)hipGetLastError();
-    fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), q.a.ptr, q.b.ptr, const_cast<void*>(q.h.ptr), p.geom,
+    fn->run(dim3(static_cast<uint32_t>(groups)), dim3(threads), a_arg, q.b.ptr, const_cast<void*>(q.h.ptr), p.geom,
             hdr, stat, hs);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(LINREC_ERR_HIP, "kernel launch: " + hip_text(e));

@@ -466,10 +466,16 @@ __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const G
 //
 // All of a is requested before any of b: a lane's requests then walk one
 // array at a time, which measured 2% faster than alternating a and b rows.
-template <typename S, int VEC, int T>
+//
+// AHEAD (decays one time step ahead, reverse only): a arrives advanced by one
+// time step, so the first position's read would be a's row L, past the batch
+// row's last.  That read is not made; the value is replaced anyway (see
+// scan_registers).
+template <typename S, int VEC, int T, bool AHEAD = false>
 __device__ __forceinline__ void load_tile(Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T], const TileSpot& s) {
 #pragma unroll
-    for (int j = 0; j < T; ++j) av[j] = load_reg<S, VEC>(s.a.r, s.a.off + j * s.a.step);
+    for (int j = 0; j < T; ++j)
+        av[j] = load_reg<S, VEC>(s.a.r, AHEAD && j == 0 && s.tau0 == 0 ? kOutOfRange : s.a.off + j * s.a.step);
 #pragma unroll
     for (int j = 0; j < T; ++j) bv[j] = load_reg<S, VEC>(s.b.r, s.b.off + j * s.b.step);
 }
@@ -477,7 +483,7 @@ __device__ __forceinline__ void load_tile(Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv
 // The pair of chunk j for one channel, composed directly from a and b: the
 // fallback when chunk j's tile has published nothing for a while.  It only
 // reads inputs, so it always finishes.
-template <typename S>
+template <typename S, bool AHEAD>
 __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               int64_t row, int64_t d, int64_t j, double& A, double& Bv) {
     A = 1.0;
@@ -486,7 +492,13 @@ __device__ inline void chunk_pair_from_inputs(const S* __restrict__ a, const S* 
     const int64_t tau_end = tau_begin + g.steps_per_tile < g.L ? tau_begin + g.steps_per_tile : g.L;
     for (int64_t tau = tau_begin; tau < tau_end; ++tau) {
         const int64_t t = time_of(g, tau);
-        const float at = (tau == 0 && g.h_init == nullptr) ? 0.0f : load_one(a + row * g.a_sb + t * g.a_sl + d);
+        // (with AHEAD, a is advanced by one time step: this read gives a at
+        // t+1, and position 0, whose decay would be a at L, takes 1 with h_init)
+        float at;
+        if constexpr (AHEAD)
+            at = tau == 0 ? (g.h_init == nullptr ? 0.0f : 1.0f) : load_one(a + row * g.a_sb + t * g.a_sl + d);
+        else
+            at = (tau == 0 && g.h_init == nullptr) ? 0.0f : load_one(a + row * g.a_sb + t * g.a_sl + d);
         const float bt = load_one(b + row * g.b_sb + t * g.b_sl + d);
         bl = __builtin_fmaf(at, bl, bt);
         A = static_cast<double>(at) * A;
@@ -531,7 +543,7 @@ constexpr bool product_in_one_word() {
 // 4-15% faster; one tile per workgroup over very long chains (over 64
 // chunks per sequence, most predecessors still pending) is fastest with 4.
 // The host picks WIN through Geometry::lookback_window.
-template <typename S, int WIN>
+template <typename S, int WIN, bool AHEAD>
 __device__ inline double lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                           int64_t row, int64_t d, const StatusArrays& st, int64_t idx, int64_t chunk,
                                           uint32_t tag_agg, uint32_t tag_inc, bool& recomputed) {
@@ -584,7 +596,7 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
         }
         // predecessor j shows nothing: compose its pair from the inputs
         double pa, pb;
-        chunk_pair_from_inputs<S>(a, b, g, row, d, j, pa, pb);
+        chunk_pair_from_inputs<S, AHEAD>(a, b, g, row, d, j, pa, pb);
         acc_b = __builtin_fma(acc_a, pb, acc_b);
         acc_a = acc_a * pa;
         recomputed = true;
@@ -654,11 +666,12 @@ struct LanePrefix {
 // along tau inside the wave, and the wave's pair into LDS.  Without h_init the
 // state before position 0 is zero, so that position's a never contributes: use
 // 0 for it.
-template <typename S, int VEC, int T, int W>
+template <typename S, int VEC, int T, int W, bool AHEAD = false>
 __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, TileShared<VEC, W>& sh, const TileSpot& s,
                                                           int lane, int wave, int quad, int grp,
                                                           Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T]) {
     if (s.tau0 == 0 && g.h_init == nullptr) set_reg<S, VEC>(av[0], 0.0f);
+    else if (AHEAD && s.tau0 == 0) set_reg<S, VEC>(av[0], 1.0f);   // h_init enters with decay 1
     if (g.h_final != nullptr) {
         // positions past L become identity steps (1, 0): they then leave the
         // state of position L-1 unchanged to the end of its lane (no stored
@@ -773,7 +786,7 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
 // for the tile's sequence: it holds the state after the workgroup's previous
 // tile of that sequence, which is the state entering this one, and receives
 // the state after this tile.
-template <typename S, int VEC, int W>
+template <typename S, int VEC, int W, bool AHEAD>
 __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
                                               uint32_t epoch, bool& recomputed, int64_t tile, double* local) {
@@ -815,8 +828,8 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                     publish(st.b + idx, tag_agg, static_cast<float>(tb));
                 }
                 h_in = g.lookback_window > 2
-                           ? lookback_channel<S, 4>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed)
-                           : lookback_channel<S, 2>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed);
+                           ? lookback_channel<S, 4, AHEAD>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed)
+                           : lookback_channel<S, 2, AHEAD>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed);
             }
             if (has_successor) publish(st.p + idx, tag_inc, static_cast<float>(__builtin_fma(ta, h_in, tb)));
         }
@@ -842,7 +855,7 @@ struct LocalCarry {
 // workgroup's next tile into (nav, nbv), scan the tile whose inputs are in
 // (av, bv), hand the wave's pair to the carry wave, and once the carry is in,
 // replay and store.
-template <typename S, int VEC, int T, int W>
+template <typename S, int VEC, int T, int W, bool AHEAD>
 __device__ __forceinline__ void data_tile(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
                                           const Geometry& g, TileShared<VEC, W>& sh, int lane, int wave, int quad,
                                           int grp, int64_t tile, Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T],
@@ -855,10 +868,10 @@ __device__ __forceinline__ void data_tile(const S* __restrict__ a, const S* __re
     {
         TileSpot ns = locate<S>(a, b, h, g, next < g.ntiles ? next : tile, wave, quad, grp, VEC, T);
         if (next >= g.ntiles) ns.a.off = ns.b.off = kOutOfRange;
-        load_tile<S, VEC, T>(nav, nbv, ns);
+        load_tile<S, VEC, T, AHEAD>(nav, nbv, ns);
     }
     const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
-    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
+    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W, AHEAD>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
     __syncthreads();   // the carry wave has written the states entering the waves
     replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);
@@ -873,7 +886,7 @@ constexpr int group_limit(int w, int vec) { return (w + vec) * kWave < 1024 ? (w
 // same number of tiles and meets the same two barriers per tile.  Carry waves
 // issue no data loads or stores, so their status polls never queue behind the
 // data traffic (loads and stores retire in order per wave).
-template <typename S, int VEC, int T, int W>
+template <typename S, int VEC, int T, int W, bool AHEAD>
 __global__ void __launch_bounds__(group_limit(W, VEC))
 scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
            Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
@@ -897,7 +910,8 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         int slot = 0;   // sequence slot of the local carry: tiles cycle through local_seqs sequences
         for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride) {
             __syncthreads();   // wave pairs are in LDS
-            carry_channel<S, VEC, W>(a, b, g, stat, sh, c, epoch, recomputed, tile, &local.h[slot][c % (kWave * VEC)]);
+            carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, c, epoch, recomputed, tile,
+                                            &local.h[slot][c % (kWave * VEC)]);
             if (g.local_seqs > 0 && ++slot == g.local_seqs) slot = 0;
             __syncthreads();   // the states entering the waves are in LDS
         }
@@ -923,14 +937,14 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
     Reg<S, VEC> a0[T], b0[T], a1[T], b1[T];
     int64_t tile = blockIdx.x;
     if (tile >= g.ntiles) return;
-    load_tile<S, VEC, T>(a0, b0, locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T));
-    data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
+    load_tile<S, VEC, T, AHEAD>(a0, b0, locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T));
+    data_tile<S, VEC, T, W, AHEAD>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
     tile += stride;
     while (tile < g.ntiles) {
-        data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a1, b1, tile + stride, a0, b0);
+        data_tile<S, VEC, T, W, AHEAD>(a, b, h, g, sh, lane, wave, quad, grp, tile, a1, b1, tile + stride, a0, b0);
         tile += stride;
         if (tile >= g.ntiles) break;
-        data_tile<S, VEC, T, W>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
+        data_tile<S, VEC, T, W, AHEAD>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
         tile += stride;
     }
 }
@@ -943,7 +957,7 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
 // its CU has no loads of its own in flight; other CUs load meanwhile (measured
 // on gfx950: one 16-wave workgroup per CU at a time, tiles starting in the
 // order their lookbacks end).
-template <typename S, int VEC, int T, int W>
+template <typename S, int VEC, int T, int W, bool AHEAD>
 __global__ void __launch_bounds__(group_limit(W, VEC))
 scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
          Geometry g, WorkspaceHeader* __restrict__ hdr, uint64_t* __restrict__ stat) {
@@ -963,7 +977,7 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         }
         bool recomputed = false;
         __syncthreads();   // wave pairs are in LDS
-        carry_channel<S, VEC, W>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile, nullptr);
+        carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile, nullptr);
         __syncthreads();   // the states entering the waves are in LDS
         if (!chained) return;
         if (__ballot(recomputed) != 0 && lane == 0)
@@ -976,8 +990,8 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
     const int grp = lane >> g.log2_lanes_d;
     const TileSpot s = locate<S>(a, b, h, g, tile, wave, quad, grp, VEC, T);
     Reg<S, VEC> av[T], bv[T];
-    load_tile<S, VEC, T>(av, bv, s);
-    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W>(g, sh, s, lane, wave, quad, grp, av, bv);
+    load_tile<S, VEC, T, AHEAD>(av, bv, s);
+    const LanePrefix<VEC> pre = scan_registers<S, VEC, T, W, AHEAD>(g, sh, s, lane, wave, quad, grp, av, bv);
     __syncthreads();   // wave pairs are in LDS
     __syncthreads();   // the states entering the waves are in LDS
     replay_store<S, VEC, T, W>(g, sh, s, wave, quad, pre, av, bv);

@@ -184,10 +184,12 @@ def _check_state(name, t, B, D, device):
         raise ValueError(f"{name} must be a contiguous float32 CUDA tensor of shape (B, D) = {(B, D)} on {device}")
 
 
-def make_desc(a, b, h, h_init=None, h_final=None, reverse=False) -> linrec_scan_desc:
-    """The linrec_scan_desc for torch tensors (no checks beyond what ctypes needs)."""
+def make_desc(a, b, h, h_init=None, h_final=None, reverse=False, a_ahead=False) -> linrec_scan_desc:
+    """The linrec_scan_desc for torch tensors (no checks beyond what ctypes needs); ``a_ahead``
+    selects the reverse form whose decays are taken one time step ahead (``reverse`` = 2)."""
     B, L, D = a.shape
-    return linrec_scan_desc(B, L, D, DTYPES[a.dtype], int(bool(reverse)), _operand(a), _operand(b), _operand(h),
+    mode = 2 if a_ahead else int(bool(reverse))
+    return linrec_scan_desc(B, L, D, DTYPES[a.dtype], mode, _operand(a), _operand(b), _operand(h),
                             None if h_init is None else h_init.data_ptr(),
                             None if h_final is None else h_final.data_ptr())
 
@@ -204,7 +206,7 @@ def _stream_ptr(stream, index: int) -> int:
     return torch.cuda.current_stream(index).cuda_stream
 
 
-def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr, workspace):
+def _enqueue(a, b, h, h_init, h_final, reverse, a_ahead, plain, stream_ptr, workspace):
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
         if plain:
@@ -212,23 +214,29 @@ def _enqueue(a, b, h, h_init, h_final, reverse, plain, stream_ptr, workspace):
             _check(_lib.linrec_scan_ws(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, ws_ptr, ws_bytes,
                                        stream_ptr))
         else:
-            desc = make_desc(a, b, h, h_init, h_final, reverse)
+            desc = make_desc(a, b, h, h_init, h_final, reverse, a_ahead)
             _check(_lib.linrec_scan_ex_ws(ctypes.byref(desc), ws_ptr, ws_bytes, stream_ptr))
     elif plain:
         B, L, D = a.size()
         _check(_lib.linrec_scan(a.data_ptr(), b.data_ptr(), h.data_ptr(), B, L, D, stream_ptr))
     else:
-        desc = make_desc(a, b, h, h_init, h_final, reverse)
+        desc = make_desc(a, b, h, h_init, h_final, reverse, a_ahead)
         _check(_lib.linrec_scan_ex(ctypes.byref(desc), stream_ptr))
 
 
 def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_final=False, reverse=False,
-                workspace=None):
+                a_ahead=False, workspace=None):
     """The channel-wise linear recurrence on the GPU.
 
     Forward (default): h[i,0,d] = a[i,0,d]*h_init[i,d] + b[i,0,d] (h_init taken as 0 when
     omitted, so h[i,0,d] = b[i,0,d]) and h[i,t,d] = a[i,t,d]*h[i,t-1,d] + b[i,t,d].
     ``reverse=True`` runs the same recurrence from t = L-1 down to 0 (h[i,t,d] uses h[i,t+1,d]).
+    ``a_ahead=True`` (with ``reverse=True``) takes each decay one time step ahead:
+    h[i,L-1,d] = h_init[i,d] + b[i,L-1,d] (0 for h_init when omitted) and
+    h[i,t,d] = a[i,t+1,d]*h[i,t+1,d] + b[i,t,d].  With an incoming gradient g as ``b`` this is
+    dLoss/db of the forward scan over ``a``, read straight from ``a`` without a shifted copy;
+    a sequence taken in pieces chains through h_init = a[:, L] * (the next piece's result at
+    its first step).
 
     ``a`` and ``b`` are CUDA tensors of shape (B, L, D), one dtype (float32, bfloat16 or
     float16), unit stride along D and any non-negative strides otherwise (views, expanded or
@@ -247,6 +255,8 @@ def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_
     fill kernel recorded in the graph before the scan, so that every replay starts from a clean
     workspace (the library itself never allocates while a stream is captured).
     """
+    if a_ahead and not reverse:
+        raise ValueError("a_ahead applies to the reverse scan (reverse=True)")
     like = _check_operand("a", a)
     _check_operand("b", b, like)
     (B, L, D), dtype, index = like
@@ -268,22 +278,22 @@ def linrec_scan(a, b, h=None, stream=None, *, h_init=None, h_final=None, return_
                                   or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous CUDA tensor on a's device")
     if workspace is None and stream is None and torch.cuda.is_current_stream_capturing():
-        need = workspace_bytes(a, b, h, h_init=h_init, h_final=h_final, reverse=reverse)
+        need = workspace_bytes(a, b, h, h_init=h_init, h_final=h_final, reverse=reverse, a_ahead=a_ahead)
         if need > 0:
             # from the capture's memory pool; torch's allocations are 512-byte aligned
             workspace = torch.zeros(need, dtype=torch.uint8, device=a.device)
     if index != torch.cuda.current_device():
         with torch.cuda.device(index):   # the library works on the current HIP device
-            _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index), workspace)
+            _enqueue(a, b, h, h_init, h_final, reverse, a_ahead, plain, _stream_ptr(stream, index), workspace)
     else:
-        _enqueue(a, b, h, h_init, h_final, reverse, plain, _stream_ptr(stream, index), workspace)
+        _enqueue(a, b, h, h_init, h_final, reverse, a_ahead, plain, _stream_ptr(stream, index), workspace)
     return (h, h_final) if want_final else h
 
 
-def workspace_bytes(a, b, h=None, *, h_init=None, h_final=None, reverse=False) -> int:
+def workspace_bytes(a, b, h=None, *, h_init=None, h_final=None, reverse=False, a_ahead=False) -> int:
     """Bytes of the lookback workspace a linrec_scan of these tensors may need on their device
     (0: none); the size a ``workspace`` argument must have."""
-    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse)
+    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse, a_ahead)
     out = ctypes.c_size_t(0)
     with torch.cuda.device(a.get_device()):
         _check(_lib.linrec_scan_ex_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))

@@ -203,7 +203,9 @@ def test_ex_rejects_bad_descriptors():
     assert lib.linrec_scan_ex(None, None) == bad
     assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, dtype=3)), None) == bad
     assert "dtype" in binding.linrec_last_error_message()
-    assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, reverse=2)), None) == bad
+    for mode in (3, -1):       # 0 forward, 1 reverse, 2 reverse with the decays one step ahead
+        assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, reverse=mode)), None) == bad
+        assert "reverse" in binding.linrec_last_error_message()
     assert lib.linrec_scan_ex(ctypes.byref(desc(2, 8, 16, strides=[(128, -16), (128, 16), (128, 16)])), None) == bad
     assert "strides" in binding.linrec_last_error_message()
     # rows of h overlap: time stride below D, or batch rows on top of each other
@@ -303,3 +305,15 @@ def test_caller_workspace_entry_points_check_sizes_before_any_hip_call():
     d.a.ptr = d.b.ptr = d.h.ptr = None
     assert lib.linrec_scan_ex_ws(ctypes.byref(d), None, 0, None) == binding.LINREC_OK
     assert lib.linrec_scan_ex_ws(None, None, 0, None) == binding.LINREC_ERR_INVALID_ARGUMENT
+
+
+def test_decays_ahead_needs_the_reverse_scan():
+    """a_ahead selects the reverse form whose decays are one time step ahead; the binding
+    refuses it for a forward scan before touching any buffer."""
+    import torch
+    x = torch.zeros(1, 4, 4)
+    with pytest.raises(ValueError, match="reverse"):
+        binding.linrec_scan(x, x, a_ahead=True)
+    d = binding.make_desc(x, x, x, reverse=True, a_ahead=True)
+    assert d.reverse == 2
+    assert binding.make_desc(x, x, x, reverse=True).reverse == 1

@@ -477,6 +477,107 @@ def test_reverse_gives_the_gradient_of_the_forward_scan(lr):
     check(da, a64.grad.numpy(), torch.float32, "gradient in a")
 
 
+def decays_ahead(a_np, last):
+    """a taken one time step ahead: a'[t] = a[t+1], and a'[L-1] = last (the decay that
+    multiplies h_init in the reverse scan: 1 when one is given; unused without one)."""
+    s = np.empty_like(a_np)
+    s[:, :-1] = a_np[:, 1:]
+    s[:, -1] = last
+    return s
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_reverse_with_decays_ahead(lr, tile, tile_env):
+    """reverse=True, a_ahead=True reads a one time step ahead inside the kernel: equal to the
+    plain reverse scan over a shifted copy of a, with and without an initial state (which enters
+    with decay 1), on ragged shapes in every tile form."""
+    set_tile(tile)
+    for k, shape in enumerate(SHAPES):
+        B, L, D = shape
+        a, b, a_np, b_np = device_inputs(shape, 1200 + k, a_lo=0.5, a_hi=1.0)
+        h = lr.linrec_scan(a, b, reverse=True, a_ahead=True)
+        torch.cuda.synchronize()
+        check(h, oracle.linrec_oracle_rev_f64(decays_ahead(a_np, 0.0), b_np), torch.float32,
+              f"decays ahead {tile or 'default'} {shape}")
+        h0_np = np.random.default_rng(1300 + k).standard_normal((B, D)).astype(np.float32)
+        h, hf = lr.linrec_scan(a, b, reverse=True, a_ahead=True, h_init=torch.from_numpy(h0_np).cuda(),
+                               return_final=True)
+        torch.cuda.synchronize()
+        ref = oracle.linrec_oracle_rev_f64(decays_ahead(a_np, 1.0), b_np, h_init=h0_np)
+        check(h, ref, torch.float32, f"decays ahead h_init {tile or 'default'} {shape}")
+        check(hf, ref[:, 0, :], torch.float32, f"decays ahead h_final {tile or 'default'} {shape}")
+
+
+@pytest.mark.parametrize("tile", ["m=0,t=4,w=8,p=32,l=0", "m=1"])
+def test_decays_ahead_through_recomputed_predecessors(lr, tile, tile_env, spin_env):
+    """With the wait for a predecessor forced to zero polls, tiles recompute their predecessors'
+    pairs from a and b: that path must take the decays one step ahead too, and a walk past
+    chunk 0 must apply h_init with decay 1.  Decays near 1 keep h_init visible over many tiles."""
+    set_tile(tile)
+    B, L, D = 2, 8192, 64
+    a, b, a_np, b_np = device_inputs((B, L, D), 1400, a_lo=0.995, a_hi=1.0)
+    h0_np = (10.0 * np.random.default_rng(1401).standard_normal((B, D))).astype(np.float32)
+    os.environ["LINREC_SPIN_LIMIT"] = "0"
+    h = lr.linrec_scan(a, b, reverse=True, a_ahead=True, h_init=torch.from_numpy(h0_np).cuda())
+    torch.cuda.synchronize()
+    os.environ.pop("LINREC_SPIN_LIMIT")
+    check(h, oracle.linrec_oracle_rev_f64(decays_ahead(a_np, 1.0), b_np, h_init=h0_np), torch.float32,
+          f"decays ahead, recomputed predecessors, {tile}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+def test_gradient_from_the_forward_decays(lr, dtype):
+    """dLoss/db of loss = sum(g * scan(a, b)), from float64 autograd of the plain recurrence on
+    the CPU, equals reverse=True, a_ahead=True over g with the forward scan's own a (no shifted
+    copy), here with a time-major a; dLoss/da[t] = dLoss/db[t] * h[t-1]."""
+    B, L, D = 2, 300, 12
+    a_np32, b_np32 = li.make_inputs(B, L, D, seed=1500, a_lo=0.5, a_hi=1.0)
+    _, g_np32 = li.make_inputs(B, L, D, seed=1501)
+    a_tm = torch.from_numpy(np.ascontiguousarray(a_np32.transpose(1, 0, 2))).cuda().to(dtype)
+    a = a_tm.transpose(0, 1)
+    b = torch.from_numpy(b_np32).cuda().to(dtype)
+    g = torch.from_numpy(g_np32).cuda().to(dtype)
+    a_np, b_np, g_np = (x.float().cpu().numpy() for x in (a, b, g))
+    a64 = torch.from_numpy(a_np).double().requires_grad_(True)
+    b64 = torch.from_numpy(b_np).double().requires_grad_(True)
+    state = torch.zeros(B, D, dtype=torch.float64)
+    rows = []
+    for t in range(L):
+        state = (a64[:, t] * state if t > 0 else 0.0) + b64[:, t]
+        rows.append(state)
+    (torch.stack(rows, dim=1) * torch.from_numpy(g_np).double()).sum().backward()
+    db = lr.linrec_scan(a, g, reverse=True, a_ahead=True)
+    h = lr.linrec_scan(a, b)
+    torch.cuda.synchronize()
+    check(db, b64.grad.numpy(), dtype, f"gradient in b, {dtype}")
+    da = torch.zeros(B, L, D, dtype=torch.float32, device="cuda")
+    da[:, 1:] = db[:, 1:].float() * h[:, :-1].float()
+    if dtype == torch.float32:
+        check(da, a64.grad.numpy(), dtype, "gradient in a")
+
+
+def test_decays_ahead_at_full_size_and_in_pieces(lr):
+    """long_sequence run backwards with the decays one step ahead (its long lookback chains),
+    whole and in three ragged pieces taken from the last: each piece starts from
+    h_init = a[:, start of the next piece] * (the next piece's result at its first step)."""
+    a_np, b_np = li.workload_inputs("long_sequence")
+    a = torch.from_numpy(a_np).cuda()
+    b = torch.from_numpy(b_np).cuda()
+    ref = oracle.linrec_oracle_rev_f64(decays_ahead(a_np, 0.0), b_np)
+    whole = lr.linrec_scan(a, b, reverse=True, a_ahead=True)
+    torch.cuda.synchronize()
+    check(whole, ref, torch.float32, "decays ahead, long_sequence")
+    L = a.shape[1]
+    cuts = [0, 70001, 200003, L]
+    pieces, state = [], None
+    for lo, hi in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        h = lr.linrec_scan(a[:, lo:hi], b[:, lo:hi], reverse=True, a_ahead=True, h_init=state)
+        pieces.append(h)
+        state = (a[:, lo] * h[:, 0]).contiguous()
+    torch.cuda.synchronize()
+    check(torch.cat(pieces[::-1], dim=1), ref, torch.float32, "decays ahead, long_sequence in pieces")
+
+
 def test_local_carry_with_every_operand_form(lr, tile_env):
     """Persistent workgroups that keep the carry local (8-lane slabs, one workgroup per CU taking
     whole sequences), with strided operands, bf16 storage, an initial and a final state, and
