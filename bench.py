@@ -124,6 +124,8 @@ def parse_args():
     p.add_argument("--dtype", default="f32", choices=["f32", "bf16", "f16"],
                    help="storage type of a, b and h (arithmetic is fp32); not f32 runs linrec_scan_ex")
     p.add_argument("--reverse", action="store_true", help="the reverse-time recurrence (linrec_scan_ex)")
+    p.add_argument("--a-ahead", action="store_true",
+                   help="with --reverse: the decays taken one time step ahead (dLoss/db of a forward scan)")
     p.add_argument("--state", action="store_true", help="pass an initial state and ask for the final state")
     p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB, at most warmup + steps)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the multi-threaded oracle baseline")
@@ -234,8 +236,16 @@ def timed_oracle(fn, a_np, b_np, h_init, threads, seconds):
 
 
 def cpu_baseline(a_np, b_np, h_last, seconds: float, single_seconds: float, shape, storage="f32", reverse=False,
-                 h_init=None):
+                 h_init=None, a_ahead=False):
     import oracle
+
+    if a_ahead:
+        # the oracle's reverse scan over the decays taken one time step ahead;
+        # the first step's decay multiplies the initial state: 1 (unused without one)
+        shifted = np.empty_like(a_np)
+        shifted[:, :-1] = a_np[:, 1:]
+        shifted[:, -1] = 1.0
+        a_np = shifted
 
     threads = oracle.default_threads()
     fn = oracle.linrec_oracle_rev_f64 if reverse else oracle.linrec_oracle_f64
@@ -345,6 +355,9 @@ def main():
     n = a_np.size
     storage = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.dtype]
     elem = 4 if args.dtype == "f32" else 2
+    if args.a_ahead and not args.reverse:
+        print("--a-ahead applies to the reverse scan: add --reverse", file=sys.stderr)
+        sys.exit(2)
     plain = args.dtype == "f32" and not args.reverse and not args.state
     # algorithmic bytes: read a and b, write h, plus the initial and final states
     step_bytes = 3 * elem * n + (8 * w.B * w.D if args.state else 0)
@@ -364,14 +377,15 @@ def main():
     hf = torch.empty((w.B, w.D), dtype=torch.float32, device="cuda") if args.state else None
     stream = torch.cuda.current_stream()
     plan = (lr.linrec_scan_plan(w.B, w.L, w.D) if plain else
-            lr.plan_for(a_sets[0], b_sets[0], h_sets[0], h_init=h0, h_final=hf, reverse=args.reverse))
+            lr.plan_for(a_sets[0], b_sets[0], h_sets[0], h_init=h0, h_final=hf, reverse=args.reverse,
+                        a_ahead=args.a_ahead))
 
     def step(k):
         if plain:
             lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream)
         else:
             lr.linrec_scan(a_sets[k], b_sets[k], h_sets[k], stream=stream, h_init=h0, h_final=hf,
-                           reverse=args.reverse)
+                           reverse=args.reverse, a_ahead=args.a_ahead)
 
     for i in range(args.warmup):
         step(i % sets)
@@ -405,7 +419,9 @@ def main():
 
     storage_name = {"f32": "fp32", "bf16": "bf16", "f16": "fp16"}[args.dtype]
     variant = "" if plain else " (linrec_scan_ex" + "".join(
-        ", " + x for x in ("reverse time" if args.reverse else "", "initial and final state" if args.state else "")
+        ", " + x for x in ("reverse time" if args.reverse else "",
+                           "decays one step ahead" if args.a_ahead else "",
+                           "initial and final state" if args.state else "")
         if x) + ")"
     headline = args.workload == li.HEADLINE and plain
     desc = w.describe(storage_name + ("" if args.dtype == "f32" else " storage, fp32 arithmetic"))
@@ -426,7 +442,7 @@ def main():
             "workload": f"{args.workload}: {desc}{variant}",
             "B": w.B, "L": w.L, "D": w.D, "seed": seed,
             "storage": args.dtype, "arithmetic": "fp32 (fp64 products of decays on the carry path)",
-            "reverse": args.reverse, "state": args.state,
+            "reverse": args.reverse, "a_ahead": args.a_ahead, "state": args.state,
             "algorithmic_bytes_per_step": step_bytes,
             "buffer_sets": sets,
             "plan": plan,
@@ -479,7 +495,7 @@ def main():
         # the oracle on the values the GPU consumed (16-bit inputs widen exactly)
         out["cpu_baseline"] = cpu_baseline(a_host.float().numpy(), b_host.float().numpy(), h_last, args.cpu_seconds,
                                            args.cpu_single_seconds, (w.B, w.L, w.D), storage=args.dtype,
-                                           reverse=args.reverse, h_init=h0_np)
+                                           reverse=args.reverse, h_init=h0_np, a_ahead=args.a_ahead)
     print(json.dumps(out), flush=True)
 
 

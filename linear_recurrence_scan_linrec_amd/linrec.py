@@ -305,9 +305,9 @@ def linrec_scan_ex_raw(desc: linrec_scan_desc, stream_ptr: int = 0) -> int:
     return _lib.linrec_scan_ex(ctypes.byref(desc), stream_ptr)
 
 
-def plan_for(a, b, h=None, *, h_init=None, h_final=None, reverse=False) -> dict:
+def plan_for(a, b, h=None, *, h_init=None, h_final=None, reverse=False, a_ahead=False) -> dict:
     """The plan linrec_scan_ex would use for these tensors (host arithmetic only)."""
-    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse)
+    desc = make_desc(a, b, a if h is None else h, h_init, h_final, reverse, a_ahead)
     plan = linrec_plan()
     _check(_lib.linrec_scan_ex_plan(ctypes.byref(desc), ctypes.byref(plan)))
     return {name: getattr(plan, name) for name, _ in linrec_plan._fields_}

@@ -53,8 +53,11 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline(monkeypatc
                                             (["--dtype", "bf16", "--reverse", "--state", "--no-cpu-baseline"],
                                              "pages_shape"),
                                             (["--dtype", "bf16", "--cpu-seconds", "0.05",
-                                              "--cpu-single-seconds", "0"], "pages_shape")],
-                         ids=["tiny", "bf16_reverse_state", "bf16_checked"])
+                                              "--cpu-single-seconds", "0"], "pages_shape"),
+                                            (["--workload", "long_sequence", "--reverse", "--a-ahead", "--state",
+                                              "--cpu-seconds", "0.05", "--cpu-single-seconds", "0"],
+                                             "long_sequence")],
+                         ids=["tiny", "bf16_reverse_state", "bf16_checked", "decays_ahead_checked"])
 def test_bench_other_workloads_and_forms(monkeypatch, capsys, extra, workload):
     monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "3", "--warmup", "1", *extra])
     print(f"bench.main: {' '.join(extra)}", flush=True)
@@ -70,8 +73,11 @@ def test_bench_other_workloads_and_forms(monkeypatch, capsys, extra, workload):
     assert r["roofline"]["traffic"] == (bench.measured_traffic(workload, dtype) if forward else None)
     if "bf16" in extra:
         assert r["config"]["storage"] == "bf16" and "bf16 storage" in r["config"]["workload"]
+    if "--a-ahead" in extra:
+        assert r["config"]["a_ahead"] is True and "decays one step ahead" in r["config"]["workload"]
     if "--no-cpu-baseline" in extra:
         assert r["cpu_baseline"] is None
     else:
-        # a 16-bit output checked against the bar with one bf16 rounding
+        # the output checked against the oracle at the storage type's bar (for the decays one step
+        # ahead: the oracle's reverse scan over a shifted copy of a, from the same initial state)
         assert r["cpu_baseline"]["gpu_check_max_bar_ratio"] <= 1.0 and "single_thread" not in r["cpu_baseline"]
