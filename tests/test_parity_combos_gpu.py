@@ -1,8 +1,9 @@
 """GPU parity on seeded combinations of the options that the other parity tests take one at a
 time: each case draws a shape (ragged L and D included), a storage type, the direction of time,
 an initial and a final state, a layout per operand (contiguous, time-major, every other time
-step of a larger tensor, broadcast over batch rows, an output inside padded rows) and a tile
-override, and compares every output element with the float64 oracle.  Same bars as the other
+step of a larger tensor, broadcast over batch rows, an output inside padded rows), a tile
+override and, for reverse scans, the decays one time step ahead, and compares every output
+element with the float64 oracle.  Same bars as the other
 linrec_scan_ex parity tests; an output's padding must stay untouched.
 """
 import numpy as np
@@ -36,7 +37,7 @@ def draw_case(k):
     D = int(rng.choice([int(rng.integers(1, 33)), int(rng.integers(33, 300)), 4 * int(rng.integers(1, 65))]))
     dtype = DTYPES[int(rng.integers(len(DTYPES)))]
     tiles = TILES + (HALF_TILES if dtype != torch.float32 else [])
-    return {
+    case = {
         "shape": (B, L, D),
         "dtype": dtype,
         "reverse": bool(rng.integers(2)),
@@ -49,6 +50,9 @@ def draw_case(k):
         "tile": tiles[int(rng.integers(len(tiles)))],
         "seed": 32000 + k,
     }
+    # drawn last, so the earlier draws of every case stay as they were
+    case["a_ahead"] = case["reverse"] and bool(rng.integers(2))
+    return case
 
 
 def lay_out(values, layout, dtype):
@@ -79,7 +83,7 @@ def test_seeded_combination(lr, k, monkeypatch):
         monkeypatch.delenv("LINREC_TILE", raising=False)
     label = (f"combo {k}: {c['shape']} {str(dtype).split('.')[-1]} tile='{c['tile']}' reverse={c['reverse']} "
              f"h_init={c['h_init']} h_final={c['h_final']} a={c['a_layout']} b={c['b_layout']} "
-             f"h_padded={c['h_padded']}")
+             f"h_padded={c['h_padded']} a_ahead={c['a_ahead']}")
     say(label)
     a_np, b_np = li.make_inputs(B, L, D, seed=c["seed"], a_lo=c["a_lo"], a_hi=1.0)
     a = lay_out(a_np, c["a_layout"], dtype)
@@ -96,8 +100,15 @@ def test_seeded_combination(lr, k, monkeypatch):
     h0_np = (np.random.default_rng(c["seed"] + 1).standard_normal((B, D)).astype(np.float32)
              if c["h_init"] else None)
     h0 = torch.from_numpy(h0_np).cuda() if c["h_init"] else None
-    out = lr.linrec_scan(a, b, h, h_init=h0, return_final=c["h_final"], reverse=c["reverse"])
+    out = lr.linrec_scan(a, b, h, h_init=h0, return_final=c["h_final"], reverse=c["reverse"],
+                         a_ahead=c["a_ahead"])
     torch.cuda.synchronize()
+    if c["a_ahead"]:
+        # the decays one time step ahead; the first step's decay multiplies h_init: 1
+        shifted = np.empty_like(a_ref)
+        shifted[:, :-1] = a_ref[:, 1:]
+        shifted[:, -1] = 1.0
+        a_ref = shifted
     fn = oracle.linrec_oracle_rev_f64 if c["reverse"] else oracle.linrec_oracle_f64
     ref = fn(a_ref, b_ref, h_init=h0_np)
     if c["h_final"]:
