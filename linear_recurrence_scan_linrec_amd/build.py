@@ -23,7 +23,8 @@ ROOT = PACKAGE.parent
 INCLUDE = ROOT / "include"
 CSRC = PACKAGE / "csrc"
 SOURCES = [CSRC / "linrec.hip", CSRC / "kernels_f32.hip", CSRC / "kernels_bf16.hip", CSRC / "kernels_f16.hip"]
-DEPENDS = SOURCES + [CSRC / "scan_kernel.hpp", CSRC / "launch.hpp", CSRC / "instances.hpp", INCLUDE / "linrec.h"]
+DEPENDS = SOURCES + [CSRC / "scan_kernel.hpp", CSRC / "call_epoch.hpp", CSRC / "launch.hpp", CSRC / "instances.hpp",
+                     INCLUDE / "linrec.h"]
 LIBRARY = PACKAGE / "lib" / "liblinrec.so"
 STREAM_SOURCES = [CSRC / "stream_ceiling.hip"]
 STREAM_LIBRARY = PACKAGE / "lib" / "libstream_ceiling.so"

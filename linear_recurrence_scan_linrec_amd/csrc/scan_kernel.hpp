@@ -530,6 +530,12 @@ constexpr bool product_in_one_word() {
     return sizeof(S) == 2;
 }
 
+// First-round-trip window of the 4-wide lookback (see lookback_channel).
+template <typename S>
+__device__ constexpr int first_window() {
+    return product_in_one_word<S>() ? 2 : 4;
+}
+
 // Decoupled lookback for one channel of a tile in chunk `chunk` (> 0): reads
 // the status of up to WIN predecessors per round trip and folds their pairs,
 // nearest first, until one of them has published its inclusive state.  A
@@ -542,8 +548,12 @@ constexpr bool product_in_one_word() {
 // other (persistent workgroups), reading 2 predecessors instead of 4 was
 // 4-15% faster; one tile per workgroup over very long chains (over 64
 // chunks per sequence, most predecessors still pending) is fastest with 4.
-// The host picks WIN through Geometry::lookback_window.
-template <typename S, int WIN, bool AHEAD>
+// The host picks WIN through Geometry::lookback_window.  FIRST (at most WIN)
+// is the window of the first round trip only: with 16-bit storage a tile's
+// life is short enough that its nearest predecessor has mostly published by
+// the time it looks back, and reading 2 there, 4 after, was 1.5-2% faster
+// on 586-chunk chains; with fp32 the same change was 0.7% slower.
+template <typename S, int WIN, bool AHEAD, int FIRST = WIN>
 __device__ inline double lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                           int64_t row, int64_t d, const StatusArrays& st, int64_t idx, int64_t chunk,
                                           uint32_t tag_agg, uint32_t tag_inc, bool& recomputed) {
@@ -551,12 +561,13 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
     double acc_a = 1.0, acc_b = 0.0;
     int64_t j = chunk - 1;                    // nearest predecessor not folded yet
     uint32_t spins = 0;
+    int reach = FIRST;                        // predecessors read this round trip
     while (j >= 0) {
         uint64_t wp[WIN], wh[WIN], wl[WIN], wb[WIN];
 #pragma unroll
         for (int m = 0; m < WIN; ++m) {
             wp[m] = wh[m] = wl[m] = wb[m] = 0;
-            if (j - m >= 0) {
+            if (j - m >= 0 && m < reach) {
                 const int64_t k = idx - (chunk - (j - m)) * stride;
                 wp[m] = observe(st.p + k);
                 wh[m] = observe(st.a_hi + k);
@@ -569,7 +580,7 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
         double h_prev = 0.0;
 #pragma unroll
         for (int m = 0; m < WIN; ++m) {
-            if (found || folded != m || j - m < 0) continue;   // stopped earlier in this window
+            if (found || folded != m || j - m < 0 || m >= reach) continue;   // stopped earlier in this window
             if (tag_of(wp[m]) == tag_inc) {
                 h_prev = payload_of(wp[m]);
                 found = true;
@@ -584,6 +595,7 @@ __device__ inline double lookback_channel(const S* __restrict__ a, const S* __re
             }
         }
         if (found) return __builtin_fma(acc_a, h_prev, acc_b);
+        reach = WIN;
         if (folded > 0) {
             j -= folded;
             spins = 0;
@@ -828,7 +840,8 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                     publish(st.b + idx, tag_agg, static_cast<float>(tb));
                 }
                 h_in = g.lookback_window > 2
-                           ? lookback_channel<S, 4, AHEAD>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed)
+                           ? lookback_channel<S, 4, AHEAD, first_window<S>()>(a, b, g, row, d, st, idx, chunk, tag_agg,
+                                                                            tag_inc, recomputed)
                            : lookback_channel<S, 2, AHEAD>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed);
             }
             if (has_successor) publish(st.p + idx, tag_inc, static_cast<float>(__builtin_fma(ta, h_in, tb)));
