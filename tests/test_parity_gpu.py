@@ -373,11 +373,34 @@ def test_graph_capture_and_replay(lr, shape):
         assert error_ratio(h_eager, oracle.linrec_oracle_f64(a_np, b_np))[0] <= TOL
 
 
+def recurrence_residual(a, b, h, steps=1 << 16):
+    """Largest |h_t - (a_t h_{t-1} + b_t)| / (1 + |h_t|) over every element, evaluated on the
+    device in float64 from the stored fp32 values, a batch row and a stretch of time steps at a
+    time; and whether h_0 = b_0 holds exactly.  Away from the hand-overs between lanes this is
+    one fp32 rounding (2^-24); where a lane starts from its carried state it is that state's
+    distance from the previous lane's last output, a few fp32 roundings of the replay.  A wrong
+    carry or a misplaced row shows up as a residual of the order of |h|."""
+    worst = 0.0
+    first_exact = True
+    B, L, _ = h.shape
+    for i in range(B):
+        first_exact &= bool(torch.equal(h[i, 0], b[i, 0]))
+        for t0 in range(1, L, steps):
+            t1 = min(L, t0 + steps)
+            ht = h[i, t0:t1].double()
+            r = (ht - (a[i, t0:t1].double() * h[i, t0 - 1:t1 - 1].double() + b[i, t0:t1].double())).abs_()
+            worst = max(worst, float((r / (1.0 + ht.abs())).max()))
+            del ht, r
+    return worst, first_exact
+
+
 @pytest.mark.parametrize("shape", [(2, 1 << 20, 1028), (16, 1 << 17, 1028)], ids=["one_tile", "persistent"])
 def test_more_than_2_31_elements(lr, shape):
     """B*L*D above 2^31 elements, with batch rows more than 2^32 bytes apart: 64-bit row and
-    status indexing.  Inputs are drawn on the device from a seeded generator (26 GB per case);
-    the oracle checks a few channels, including the last slab's ragged edge, over every step."""
+    status indexing.  Inputs are drawn on the device from a seeded generator (26 GB per case).
+    Every element is checked against the recurrence itself (the residual of each step from the
+    stored values, far below the bar), and the oracle checks a few channels, including the last
+    slab's ragged edge, over every step."""
     B, L, D = shape
     assert B * L * D > 2 ** 31
     say(f"[large] {shape}: {B * L * D} elements")
@@ -387,6 +410,10 @@ def test_more_than_2_31_elements(lr, shape):
     b = torch.randn(shape, device="cuda", generator=gen)
     h = lr.linrec_scan(a, b)
     torch.cuda.synchronize()
+    residual, first_exact = recurrence_residual(a, b, h)
+    say(f"[large] {shape}: largest step residual {residual:.3e}, h_0 = b_0: {first_exact}")
+    assert first_exact
+    assert residual <= TOL / 4, residual
     cols = [0, 5, 511, D - 4, D - 1]
     a_s = np.ascontiguousarray(a[:, :, cols].cpu().numpy())
     b_s = np.ascontiguousarray(b[:, :, cols].cpu().numpy())
