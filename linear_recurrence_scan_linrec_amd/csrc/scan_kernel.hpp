@@ -402,8 +402,9 @@ __device__ __forceinline__ int64_t sequence_of(const Geometry& g, int64_t slot) 
 }
 
 // Tile index -> (chunk, sequence, batch row, slab).  The operands are
-// wave-uniform, so each division is a scalar instruction sequence on the
-// tile's critical path.  Tiles number fewer than 2^31 (the host refuses more),
+// wave-uniform, so each division is a long scalar instruction sequence (the
+// carry waves therefore run it before the barrier that starts their part of
+// a tile).  Tiles number fewer than 2^31 (the host refuses more),
 // so the 32-bit form is exact.  Measured on MI355X, same-run A/B: with 16-bit
 // storage, whose tiles move half the bytes, the 32-bit form is 2-10% faster;
 // with fp32 storage the 64-bit form is 3-10% faster on the local-carry plans
@@ -801,9 +802,10 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
 template <typename S, int VEC, int W, bool AHEAD>
 __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
-                                              uint32_t epoch, bool& recomputed, int64_t tile, double* local) {
+                                              uint32_t epoch, bool& recomputed, int64_t tile, const TileIndex* early,
+                                              double* local) {
     if (c >= g.slab_channels) return;
-    const TileIndex ix = tile_index<S>(g, tile);
+    const TileIndex ix = early != nullptr ? *early : tile_index<S>(g, tile);
     const int64_t chunk = ix.chunk, seq = ix.seq, row = ix.row, slab = ix.slab;
     const int64_t d = slab * g.slab_channels + c;
     const double* pair_a = &sh.pair_a[0][0].v[0];
@@ -922,9 +924,22 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         bool recomputed = false;
         int slot = 0;   // sequence slot of the local carry: tiles cycle through local_seqs sequences
         for (int64_t tile = blockIdx.x; tile < g.ntiles; tile += stride) {
-            __syncthreads();   // wave pairs are in LDS
-            carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, c, epoch, recomputed, tile,
-                                            &local.h[slot][c % (kWave * VEC)]);
+            // The tile's decomposition is a long instruction sequence.  With at
+            // most 2 data waves every wave of the workgroup has a SIMD of its
+            // own, so it runs while the data waves scan instead of between the
+            // barriers, where they wait for it (measured: 2-3% off the B=32
+            // L=4096 D=256 and B=8 L=16384 D=1024 fp32 scans).  With more data
+            // waves the carry waves share their SIMDs, and there it cost the
+            // data waves about 1% (B=16 L=512 D=8192).
+            double* cell = &local.h[slot][c % (kWave * VEC)];
+            if constexpr (W <= 2) {
+                const TileIndex ix = tile_index<S>(g, tile);
+                __syncthreads();   // wave pairs are in LDS
+                carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, c, epoch, recomputed, tile, &ix, cell);
+            } else {
+                __syncthreads();   // wave pairs are in LDS
+                carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, c, epoch, recomputed, tile, nullptr, cell);
+            }
             if (g.local_seqs > 0 && ++slot == g.local_seqs) slot = 0;
             __syncthreads();   // the states entering the waves are in LDS
         }
@@ -989,8 +1004,9 @@ scan_one(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
             if (carry == 0) before = count_in(hdr, epoch, lane);
         }
         bool recomputed = false;
+        const TileIndex ix = tile_index<S>(g, tile);   // while the data waves wait for their loads
         __syncthreads();   // wave pairs are in LDS
-        carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile, nullptr);
+        carry_channel<S, VEC, W, AHEAD>(a, b, g, stat, sh, carry * kWave + lane, epoch, recomputed, tile, &ix, nullptr);
         __syncthreads();   // the states entering the waves are in LDS
         if (!chained) return;
         if (__ballot(recomputed) != 0 && lane == 0)
