@@ -685,10 +685,12 @@ __device__ __forceinline__ LanePrefix<VEC> scan_registers(const Geometry& g, Til
                                                           Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T]) {
     if (s.tau0 == 0 && g.h_init == nullptr) set_reg<S, VEC>(av[0], 0.0f);
     else if (AHEAD && s.tau0 == 0) set_reg<S, VEC>(av[0], 1.0f);   // h_init enters with decay 1
-    if (g.h_final != nullptr) {
-        // positions past L become identity steps (1, 0): they then leave the
-        // state of position L-1 unchanged to the end of its lane (no stored
-        // output depends on them either way)
+    if (g.h_final != nullptr && (s.chunk + 1) * g.steps_per_tile > g.L) {
+        // positions past L (only the last chunk of a ragged length has them;
+        // the test is uniform, so other tiles skip the per-lane checks)
+        // become identity steps (1, 0): they then leave the state of position
+        // L-1 unchanged to the end of its lane (no stored output depends on
+        // them either way)
 #pragma unroll
         for (int j = 0; j < T; ++j) {
             if (s.tau0 + j >= g.L) {
