@@ -135,6 +135,9 @@ def parse_args():
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
     p.add_argument("--ceiling-shape", metavar="R,U,G",
                    help="run the ceiling only in this walk (rows R), unroll U and groups per CU G (for counter runs)")
+    p.add_argument("--stream-rows", metavar="R1,R2,...",
+                   help="no scan: time the read-2-write-1 stream over this workload's buffers walking R batch-row "
+                        "streams at once (R = 1: one contiguous sweep), best launch shape per R; prints one JSON line")
     p.add_argument("--regions", type=int, default=10,
                    help="further regions of 10 launches whose means give median/p10/p90 (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,30 +307,48 @@ def measure_ceiling(torch, xs, ys, zs, rows: int, stream, warmup=3, reps=10, onl
     """Best mean launch time (us) of the read-2-write-1 stream over the given buffers (any storage,
     reinterpreted as float32) for each walk order; returns {order: {...}}.  ``only`` = (R, U, G)
     restricts the sweep to one walk and launch shape."""
-    from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
-
-    flat = lambda t: t.reshape(-1).view(torch.float32)  # noqa: E731
-    X, Y, Z = [flat(t) for t in xs], [flat(t) for t in ys], [flat(t) for t in zs]
-    n = X[0].numel()
     out = {}
     orders = (("contiguous", 1), ("scan_order", rows))
     if only is not None:
         orders = (("contiguous" if only[0] == 1 else "scan_order", only[0]),)
     for order, r in orders:
-        best = None
-        for unroll in ((1, 2, 4) if only is None else (only[1],)):
-            if n % (r * 256 * unroll) != 0:
-                continue
-            for gpc in ((1, 2, 4, 8) if only is None else (only[2],)):
-                def launch(k, r=r, unroll=unroll, gpc=gpc):
-                    sc.stream_r2w1(X[k % len(X)], Y[k % len(X)], Z[k % len(X)], r, unroll, gpc, stream)
-                for k in range(warmup):
-                    launch(k)
-                us = region_mean_us(torch, launch, reps, stream, first=warmup)
-                if best is None or us < best["us"]:
-                    best = {"us": round(us, 3), "rows": r, "unroll": unroll, "groups_per_cu": gpc}
+        best = sweep_walk(torch, xs, ys, zs, r, stream, warmup, reps,
+                          (1, 2, 4) if only is None else (only[1],), (1, 2, 4, 8) if only is None else (only[2],))
         if best is not None:
             out[order] = best
+    return out
+
+
+def sweep_walk(torch, xs, ys, zs, r, stream, warmup, reps, unrolls, groups):
+    """Best mean launch time of the stream walking r row streams, over the given launch shapes."""
+    from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
+
+    flat = lambda t: t.reshape(-1).view(torch.float32)  # noqa: E731
+    X, Y, Z = [flat(t) for t in xs], [flat(t) for t in ys], [flat(t) for t in zs]
+    n = X[0].numel()
+    best = None
+    for unroll in unrolls:
+        if n % (r * 256 * unroll) != 0:
+            continue
+        for gpc in groups:
+            def launch(k, unroll=unroll, gpc=gpc):
+                sc.stream_r2w1(X[k % len(X)], Y[k % len(X)], Z[k % len(X)], r, unroll, gpc, stream)
+            for k in range(warmup):
+                launch(k)
+            us = region_mean_us(torch, launch, reps, stream, first=warmup)
+            if best is None or us < best["us"]:
+                best = {"us": round(us, 3), "rows": r, "unroll": unroll, "groups_per_cu": gpc}
+    return best
+
+
+def stream_rows(torch, xs, ys, zs, rows_list, stream, workload, nbytes):
+    """The read-2-write-1 stream over the same buffers for each number of concurrent row streams:
+    best mean launch time over unroll x groups per CU (the ceiling's own sweep)."""
+    out = {"kind": "stream_rows", "workload": workload, "bytes_per_launch": nbytes, "rows": {}}
+    for r in rows_list:
+        b = sweep_walk(torch, xs, ys, zs, r, stream, 3, 10, (1, 2, 4), (1, 2, 4, 8))
+        if b is not None:
+            out["rows"][str(r)] = dict(b, gbs=round(nbytes / (b["us"] * 1e-6) / 1e9, 1))
     return out
 
 
@@ -376,6 +397,10 @@ def main():
     h0 = torch.from_numpy(h0_np).cuda() if args.state else None
     hf = torch.empty((w.B, w.D), dtype=torch.float32, device="cuda") if args.state else None
     stream = torch.cuda.current_stream()
+    if args.stream_rows:
+        print(json.dumps(stream_rows(torch, a_sets, b_sets, h_sets, [int(r) for r in args.stream_rows.split(",")],
+                                     stream, args.workload, 3 * elem * n)))
+        return
     plan = (lr.linrec_scan_plan(w.B, w.L, w.D) if plain else
             lr.plan_for(a_sets[0], b_sets[0], h_sets[0], h_init=h0, h_final=hf, reverse=args.reverse,
                         a_ahead=args.a_ahead))
