@@ -81,3 +81,20 @@ def test_bench_other_workloads_and_forms(monkeypatch, capsys, extra, workload):
         # the output checked against the oracle at the storage type's bar (for the decays one step
         # ahead: the oracle's reverse scan over a shifted copy of a, from the same initial state)
         assert r["cpu_baseline"]["gpu_check_max_bar_ratio"] <= 1.0 and "single_thread" not in r["cpu_baseline"]
+
+
+def test_stream_rows_mode(monkeypatch, capsys):
+    """--stream-rows times only the read-2-write-1 stream, once per row count, and prints one JSON
+    line: contiguous (R = 1) and the scan's 32-row order of the headline buffers."""
+    monkeypatch.setattr("sys.argv", ["bench.py", "--steps", "1", "--warmup", "1", "--stream-rows", "1,32"])
+    print("bench.main: --stream-rows 1,32", flush=True)
+    bench.main()
+    lines = [line for line in capsys.readouterr().out.splitlines() if line.startswith("{")]
+    assert len(lines) == 1
+    r = json.loads(lines[0])
+    assert r["kind"] == "stream_rows" and r["workload"] == "pages_shape"
+    assert r["bytes_per_launch"] == 12 * 32 * 4096 * 256
+    assert sorted(r["rows"]) == ["1", "32"]
+    for key, rec in r["rows"].items():
+        assert rec["rows"] == int(key) and rec["us"] > 0
+        assert rec["gbs"] == pytest.approx(r["bytes_per_launch"] / rec["us"] / 1e3, rel=1e-3)
