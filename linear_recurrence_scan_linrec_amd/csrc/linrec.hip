@@ -362,8 +362,9 @@ linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     }
     p.tiles = tiles;
     g.ntiles = tiles;
-    // lookback window: 4 predecessors per round trip only for one tile per
-    // workgroup over long chains, else 2 (see lookback_channel)
+    // lookback window: the wider long-chain window (3 predecessors per round
+    // trip in fp32, 4 in 16 bits) only for one tile per workgroup over long
+    // chains, else 2 (see lookback_channel)
     g.lookback_window = (s.m == 1 && g.nchunks > 64) ? 4 : 2;
     if (g.nchunks > 1) {
         g.nstatus = tiles * g.slab_channels;

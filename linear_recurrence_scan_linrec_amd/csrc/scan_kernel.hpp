@@ -109,7 +109,7 @@ struct Geometry {
                            // workgroup's own tile local_seqs tiles earlier and the carry stays in
                            // LDS (no status words, no workspace); 0: decoupled lookback
     int32_t line_shift;    // log2 of the slabs that share one 128-byte line (0: slots are sequences)
-    int32_t lookback_window;  // predecessors a lookback reads per round trip: 2 or 4
+    int32_t lookback_window;  // 2: read 2 predecessors per round trip; above 2: the long-chain window
 };
 
 template <int VEC> struct Vec { float v[VEC]; };
@@ -531,10 +531,15 @@ constexpr bool product_in_one_word() {
     return sizeof(S) == 2;
 }
 
-// First-round-trip window of the 4-wide lookback (see lookback_channel).
+// The long-chain lookback window (see lookback_channel): predecessors read per
+// round trip, and on the first round trip.
+template <typename S>
+__device__ constexpr int long_window() {
+    return product_in_one_word<S>() ? 4 : 3;
+}
 template <typename S>
 __device__ constexpr int first_window() {
-    return product_in_one_word<S>() ? 2 : 4;
+    return product_in_one_word<S>() ? 2 : 3;
 }
 
 // Decoupled lookback for one channel of a tile in chunk `chunk` (> 0): reads
@@ -544,16 +549,20 @@ __device__ constexpr int first_window() {
 // recomputed from the inputs (`recomputed` is set).  Returns the state that
 // enters the tile.
 //
-// The window trades status reads against round trips.  Measured on MI355X
-// (same-run A/B): where the tiles of a chunk-major round look back at each
-// other (persistent workgroups), reading 2 predecessors instead of 4 was
-// 4-15% faster; one tile per workgroup over very long chains (over 64
-// chunks per sequence, most predecessors still pending) is fastest with 4.
-// The host picks WIN through Geometry::lookback_window.  FIRST (at most WIN)
-// is the window of the first round trip only: with 16-bit storage a tile's
-// life is short enough that its nearest predecessor has mostly published by
-// the time it looks back, and reading 2 there, 4 after, was 1.5-2% faster
-// on 586-chunk chains; with fp32 the same change was 0.7% slower.
+// The window trades status reads against round trips: each status word read
+// costs time of its own (one more inclusive-state word per round trip made
+// 586-chunk chains 1-4% slower).  Measured on MI355X (same-run A/B): where
+// the tiles of a chunk-major round look back at each other (persistent
+// workgroups), reading 2 predecessors instead of 4 was 4-15% faster; one tile
+// per workgroup over very long chains (over 64 chunks per sequence, most
+// predecessors still pending) wants a wider window: 3 with fp32 storage (1.5%
+// faster than 4), 4 with 16-bit storage, whose tiles publish the product of
+// decays in one word (3 was no faster).  The host picks the long-chain form
+// through Geometry::lookback_window.  FIRST (at most WIN) is the window of the
+// first round trip only: with 16-bit storage a tile's life is short enough
+// that its nearest predecessor has mostly published by the time it looks
+// back, and reading 2 there, 4 after, was 1.5-2% faster on 586-chunk chains;
+// with fp32, 2 then 4 was 0.7% slower than 4 throughout.
 template <typename S, int WIN, bool AHEAD, int FIRST = WIN>
 __device__ inline double lookback_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                           int64_t row, int64_t d, const StatusArrays& st, int64_t idx, int64_t chunk,
@@ -844,8 +853,8 @@ __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* 
                     publish(st.b + idx, tag_agg, static_cast<float>(tb));
                 }
                 h_in = g.lookback_window > 2
-                           ? lookback_channel<S, 4, AHEAD, first_window<S>()>(a, b, g, row, d, st, idx, chunk, tag_agg,
-                                                                            tag_inc, recomputed)
+                           ? lookback_channel<S, long_window<S>(), AHEAD, first_window<S>()>(
+                                 a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed)
                            : lookback_channel<S, 2, AHEAD>(a, b, g, row, d, st, idx, chunk, tag_agg, tag_inc, recomputed);
             }
             if (has_successor) publish(st.p + idx, tag_inc, static_cast<float>(__builtin_fma(ta, h_in, tb)));
