@@ -269,7 +269,8 @@ def test_spin_limit_zero_recomputes_and_stays_exact(lr, spin_env, tile_env, m):
     status not yet published recomputes that predecessor's pair from a and b.  The output must not
     change beyond the bar, and every kernel exits normally."""
     os.environ["LINREC_TILE"] = f"m={m}"
-    for shape, lo in (((2, 8192, 64), 0.9), ((4, 2048, 256), 0.0)):
+    # (2, 40000, 64) with one tile per workgroup: 90 chunks per sequence, the long-chain window
+    for shape, lo in (((2, 8192, 64), 0.9), ((4, 2048, 256), 0.0), ((2, 40000, 64), 0.9)):
         a_np, b_np = li.make_inputs(*shape, seed=9, a_lo=lo, a_hi=1.0)
         ref = oracle.linrec_oracle_f64(a_np, b_np)
         before = lr.linrec_device_timeouts()
