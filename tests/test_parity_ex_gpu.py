@@ -401,6 +401,32 @@ def test_recompute_with_initial_state(lr, tile, reverse, tile_env, spin_env):
     check(hf, ref[:, 0 if reverse else -1, :], torch.float32, label + " h_final")
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16], ids=["f32", "bf16", "f16"])
+def test_recompute_on_long_chains(lr, dtype, tile_env, spin_env):
+    """The long-chain lookback window (one tile per workgroup, 90 chunks per sequence: 3
+    predecessors per round trip in fp32, 2 then 4 in 16 bits) with the wait forced to zero polls,
+    with an initial state that decays near 1 keep visible over many tiles, so that recomputed
+    pairs and walks past chunk 0 both reach the output."""
+    set_tile("")
+    B, L, D = 2, 40000, 64
+    a, b, a_np, b_np = device_inputs((B, L, D), 720, dtype, a_lo=0.995, a_hi=1.0)
+    h0_np = (10.0 * np.random.default_rng(721).standard_normal((B, D))).astype(np.float32)
+    h0 = torch.from_numpy(h0_np).cuda()
+    plan = lr.plan_for(a, b, h_init=h0)
+    assert plan["mode"] == 1 and plan["chunks"] > 64, plan
+    before = lr.linrec_device_timeouts()
+    os.environ["LINREC_SPIN_LIMIT"] = "0"
+    h, hf = lr.linrec_scan(a, b, h_init=h0, return_final=True)
+    torch.cuda.synchronize()
+    os.environ.pop("LINREC_SPIN_LIMIT")
+    recomputed = lr.linrec_device_timeouts() - before
+    ref = oracle.linrec_oracle_f64(a_np, b_np, h_init=h0_np)
+    label = f"long-chain recompute {dtype} ({recomputed} tiles recomputed)"
+    check(h, ref, dtype, label)
+    check(hf, ref[:, -1, :], torch.float32, label + " h_final")
+    assert recomputed > 0
+
+
 # ----------------------------------------------------------------------------- reverse time
 
 @pytest.mark.parametrize("tile", TILES)
