@@ -549,9 +549,9 @@ __device__ constexpr int first_window() {
 // recomputed from the inputs (`recomputed` is set).  Returns the state that
 // enters the tile.
 //
-// The window trades status reads against round trips: each status word read
-// costs time of its own (one more inclusive-state word per round trip made
-// 586-chunk chains 1-4% slower).  Measured on MI355X (same-run A/B): where
+// The window trades status reads against round trips, and status reads are
+// not free (one more inclusive-state word per round trip made 586-chunk
+// chains 1-4% slower).  Measured on MI355X (same-run A/B): where
 // the tiles of a chunk-major round look back at each other (persistent
 // workgroups), reading 2 predecessors instead of 4 was 4-15% faster; one tile
 // per workgroup over very long chains (over 64 chunks per sequence, most
@@ -809,7 +809,8 @@ __device__ __forceinline__ void replay_store(const Geometry& g, const TileShared
 // With a local carry (g.local_seqs > 0), `local` is this channel's LDS cell
 // for the tile's sequence: it holds the state after the workgroup's previous
 // tile of that sequence, which is the state entering this one, and receives
-// the state after this tile.
+// the state after this tile.  `early`, when given, is the tile's
+// decomposition, computed by the caller before the barrier.
 template <typename S, int VEC, int W, bool AHEAD>
 __device__ __forceinline__ void carry_channel(const S* __restrict__ a, const S* __restrict__ b, const Geometry& g,
                                               uint64_t* __restrict__ stat, TileShared<VEC, W>& sh, int c,
