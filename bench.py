@@ -21,9 +21,9 @@ After the timed region (never inside it):
   scan's order over batch rows, each the best of a small sweep of launch
   shapes timed the same way; ``frac_of_ceiling`` is the scan's achieved rate
   over the contiguous stream's.
-* ``--cold N``: N single launches, each after a 1 GiB write that evicts the
-  caches, and N single warm launches, each with its own event pair (so both
-  carry the same per-pair overhead and compare with each other).
+* ``--cold N`` (default 10): N single launches, each after a 1 GiB write that
+  evicts the caches, and N single warm launches, each with its own event pair
+  (so both carry the same per-pair overhead and compare with each other).
 * the CPU baseline: the float64 oracle on the same host arrays for a bounded
   number of seconds, multi-threaded and single-threaded, and a check of the
   last GPU output against it at the storage type's bar.
@@ -130,8 +130,9 @@ def parse_args():
     p.add_argument("--sets", type=int, default=0, help="input/output copies to rotate (0: enough for >= 1 GB, at most warmup + steps)")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the multi-threaded oracle baseline")
     p.add_argument("--cpu-single-seconds", type=float, default=5.0, help="time budget of the single-threaded oracle pass")
-    p.add_argument("--cold", type=int, default=0, metavar="N",
-                   help="after the timed steps, N launches each preceded by a cache-evicting write (untimed)")
+    p.add_argument("--cold", type=int, default=10, metavar="N",
+                   help="after the timed steps, N launches each preceded by a cache-evicting write, and N warm "
+                        "ones, each with its own event pair (not part of the timed region; 0: none)")
     p.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling sweep")
     p.add_argument("--ceiling-shape", metavar="R,U,G",
                    help="run the ceiling only in this walk (rows R), unroll U and groups per CU G (for counter runs)")
