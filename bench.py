@@ -21,6 +21,12 @@ After the timed region (never inside it):
   scan's order over batch rows, each the best of a small sweep of launch
   shapes timed the same way; ``frac_of_ceiling`` is the scan's achieved rate
   over the contiguous stream's.
+* ``ceiling.tile_walk`` (fp32 local-carry plans of one sequence per
+  workgroup): the same stream in the plan's own tile walk
+  (linrec_stream_column_walk: one workgroup per (batch row, channel slab)
+  sequence, the plan's waves and rows per lane, two barriers per tile) over the
+  same buffers, and the scan's rate over it; ``--walk-shapes`` times other walk
+  shapes instead.
 * ``--cold N`` (default 10): N single launches, each after a 1 GiB write that
   evicts the caches, and N single warm launches, each with its own event pair
   (so both carry the same per-pair overhead and compare with each other).
@@ -139,6 +145,9 @@ def parse_args():
     p.add_argument("--stream-rows", metavar="R1,R2,...",
                    help="no scan: time the read-2-write-1 stream over this workload's buffers walking R batch-row "
                         "streams at once (R = 1: one contiguous sweep), best launch shape per R; prints one JSON line")
+    p.add_argument("--walk-shapes", metavar="P,W,T;...",
+                   help="time the stream in these tile walks (lanes per row P, waves W, rows per lane T) instead of "
+                        "the plan's own")
     p.add_argument("--regions", type=int, default=10,
                    help="further regions of 10 launches whose means give median/p10/p90 (0: none)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -342,6 +351,24 @@ def sweep_walk(torch, xs, ys, zs, r, stream, warmup, reps, unrolls, groups):
     return best
 
 
+def measure_tile_walk(torch, xs, ys, zs, shape, walks, stream, warmup=3, reps=10):
+    """Mean launch time (us) of the read-2-write-1 stream in each tile walk (lanes, waves, rows per
+    lane) over the given fp32 (B, L, D) buffers; returns a list of {...}."""
+    from linear_recurrence_scan_linrec_amd import stream_ceiling as sc
+
+    B, L, D = shape
+    out = []
+    for lanes, waves, t in walks:
+        def launch(k, lanes=lanes, waves=waves, t=t):
+            j = k % len(xs)
+            sc.column_walk(xs[j], ys[j], zs[j], B, L, D, lanes, waves, t, stream)
+        for k in range(warmup):
+            launch(k)
+        us = region_mean_us(torch, launch, reps, stream, first=warmup)
+        out.append({"us": round(us, 3), "lanes": lanes, "waves": waves, "steps_per_lane": t})
+    return out
+
+
 def stream_rows(torch, xs, ys, zs, rows_list, stream, workload, nbytes):
     """The read-2-write-1 stream over the same buffers for each number of concurrent row streams:
     best mean launch time over unroll x groups per CU (the ceiling's own sweep)."""
@@ -499,6 +526,21 @@ def main():
         if "contiguous" in ceil:
             out["ceiling_gbs"] = ceil["contiguous"]["gbs"]
             out["frac_of_ceiling"] = round(achieved / ceil["contiguous"]["gbs"], 4) if not args.state else None
+        walks = ([tuple(int(v) for v in x.split(",")) for x in args.walk_shapes.split(";")] if args.walk_shapes else
+                 [(plan["lanes_per_row"], plan["waves"], plan["steps_per_lane"])])
+        # the plan's own walk when it is one sequence per workgroup: a local carry whose grid is
+        # the sequences themselves (from the CU count up to twice it)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        lanes = plan["lanes_per_row"]
+        nseq = w.B * (w.D // (4 * lanes)) if lanes >= 8 and w.D % (4 * lanes) == 0 else 0
+        own = (args.dtype == "f32" and plan["mode"] == 0 and plan["vec"] == 4 and cus <= nseq < 2 * cus
+               and plan["waves"] in (1, 2, 4, 8) and plan["steps_per_lane"] in (4, 8))
+        if only is None and args.dtype == "f32" and (own or args.walk_shapes):
+            tw = measure_tile_walk(torch, a_sets, b_sets, h_sets, (w.B, w.L, w.D), walks, stream)
+            for v in tw:
+                v["gbs"] = round(3 * elem * n / (v["us"] * 1e-6) / 1e9, 1)
+                v["frac_scan"] = round(achieved / v["gbs"], 4) if not args.state else None
+            out["ceiling"]["tile_walk"] = tw[0] if len(tw) == 1 else tw
     if args.cold > 0:
         flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
         cold, warm = [], []

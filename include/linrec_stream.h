@@ -47,6 +47,28 @@ extern "C" {
 int linrec_stream_r2w1(const float *x, const float *y, float *z, int64_t n, int64_t rows, int32_t unroll,
                        int32_t groups_per_cu, void *stream);
 
+/*
+ * linrec_stream_column_walk -- enqueue z = x + y over three (B, L, D) fp32
+ * arrays (contiguous, D fastest) in the walk of the scan's local-carry plans:
+ * one workgroup per (batch row, slab of 4 * lanes channels) sequence, `waves`
+ * waves whose lanes each take 4 channels and `steps_per_lane` consecutive rows,
+ * tiles of waves * (64 / lanes) * steps_per_lane rows taken in order along L
+ * with the next tile's loads in flight, and two workgroup barriers per tile.
+ *
+ *   lanes            8, 16, 32 or 64 (slabs of 128, 256, 512 or 1024 bytes);
+ *                    D a multiple of 4 * lanes.
+ *   waves            1, 2, 4 or 8.
+ *   steps_per_lane   4 or 8.
+ *   (L + 512) * D * 4 bytes must stay below 2 GiB (one batch row of an array,
+ *                    and the rows a tile reaches past its end).
+ *   Buffers as for linrec_stream_r2w1 (16-byte aligned, z disjoint from x, y).
+ *
+ * Returns 0 when enqueued (also for an empty shape), 1 for invalid arguments,
+ * 2 for a HIP error.  Nothing is allocated.
+ */
+int linrec_stream_column_walk(const float *x, const float *y, float *z, int64_t B, int64_t L, int64_t D,
+                              int32_t lanes, int32_t waves, int32_t steps_per_lane, void *stream);
+
 /* Text of the calling thread's last failure ("" if none). */
 const char *linrec_stream_last_error(void);
 

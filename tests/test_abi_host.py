@@ -55,6 +55,22 @@ def test_stream_ceiling_library_exports_and_checks_arguments():
     assert f(base + 4, base + 8192, base + 65536, 1024, 1, 1, 2, None) == 1  # misaligned
     assert b"aligned" in lib.linrec_stream_last_error()
 
+    c = lib.linrec_stream_column_walk
+    assert c(None, None, None, 0, 4096, 256, 8, 2, 8, None) == 0             # empty: no-op
+    assert c(None, None, None, 32, 4096, 256, 4, 2, 8, None) == 1            # lanes
+    assert b"lanes" in lib.linrec_stream_last_error()
+    assert c(None, None, None, 32, 4096, 256, 8, 3, 8, None) == 1            # waves
+    assert c(None, None, None, 32, 4096, 256, 8, 2, 16, None) == 1           # steps per lane
+    assert c(None, None, None, 32, 4096, 100, 8, 2, 8, None) == 1            # D not whole slabs
+    assert c(None, None, None, 1, 1 << 20, 1024, 8, 2, 8, None) == 1         # a batch row past 2 GiB
+    assert b"2 GiB" in lib.linrec_stream_last_error()
+    assert c(None, None, None, 32, 4096, 256, 8, 2, 8, None) == 1            # null buffers
+    n = 32 * 4096 * 256 * 4
+    assert c(base, base + 2 * n, base + 16, 32, 4096, 256, 8, 2, 8, None) == 1   # z overlaps x
+    assert b"overlaps" in lib.linrec_stream_last_error()
+    assert c(base + 4, base + 2 * n, base + 4 * n, 32, 4096, 256, 8, 2, 8, None) == 1   # misaligned
+    assert b"aligned" in lib.linrec_stream_last_error()
+
 
 def test_status_strings():
     assert binding.linrec_status_string(0) == "success"
