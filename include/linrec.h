@@ -133,8 +133,9 @@ typedef struct linrec_plan {
 /*
  * linrec_scan_plan -- fills *plan for a linrec_scan of shape (B, L, D) whose
  * buffers are 16-byte aligned (aligned16 != 0) or not, on a 256-CU MI355X.
- * Pure host arithmetic, no HIP call.  Returns LINREC_ERR_INVALID_ARGUMENT for negative or
- * overflowing sizes, an unsupported LINREC_TILE or a null plan.
+ * Pure host arithmetic, no HIP call.  Returns LINREC_ERR_INVALID_ARGUMENT for negative sizes,
+ * B*L*D*8 beyond 2^63 - 1 (every entry point applies this limit), more than 2^31 - 1 tiles,
+ * an unsupported LINREC_TILE or a null plan.
  */
 linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan *plan);
 
@@ -175,8 +176,14 @@ typedef struct linrec_operand {
  *             The backward forms are not on the pages that define the forward
  *             recurrence.
  *   a, b, h   operands; h.ptr is written (cast away its const).  h's rows
- *             (i, t) must not overlap one another, and h must not overlap a
- *             or b (a and b may overlap each other).
+ *             (i, t) must not overlap one another, checked as nesting: taking
+ *             h's batch and time dimensions in increasing stride, each stride
+ *             (of a dimension longer than 1) is at least the elements that one
+ *             row and the smaller dimension span.  Contiguous, padded and
+ *             transposed layouts nest; a layout whose time rows interleave
+ *             with its batch rows is refused even where no two rows share an
+ *             element.  h must not overlap a or b (a and b may overlap each
+ *             other).
  *   h_init    NULL, or a (B, D) row-major fp32 device buffer: the state before
  *             the first step of the scan order, so that the first step is
  *             h = a * h_init + b instead of h = b (forward: t = 0; reverse:

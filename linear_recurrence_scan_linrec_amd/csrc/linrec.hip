@@ -266,7 +266,7 @@ linrec_status make_problem(const linrec_scan_desc* d, Problem& p) {
     p.es = element_bytes(q.dtype);
     int64_t n = 0, bl = 0;
     if (!checked_mul(q.B, q.L, bl) || !checked_mul(bl, q.D, n) || n > INT64_MAX / 8)
-        return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D elements overflow");
+        return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D elements overflow (B*L*D*8 must fit in 63 bits)");
     if (!operand_extent(q.a, q.B, q.L, q.D, p.es, p.extent_a) || !operand_extent(q.b, q.B, q.L, q.D, p.es, p.extent_b) ||
         !operand_extent(q.h, q.B, q.L, q.D, p.es, p.extent_h))
         return fail(LINREC_ERR_INVALID_ARGUMENT, "an operand's strides reach beyond 2^63 bytes");
@@ -810,7 +810,7 @@ extern "C" {
 
 linrec_status linrec_scan_plan(int64_t B, int64_t L, int64_t D, int aligned16, linrec_plan* plan) {
     if (plan == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "plan is null");
-    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0 and B*L*D*4 bytes fit");
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0 and B*L*D*8 must fit in 63 bits");
     // stand-in addresses with the alignment asked about; nothing is dereferenced
     const float* base = reinterpret_cast<const float*>(aligned16 ? uintptr_t(256) : uintptr_t(260));
     const linrec_scan_desc d = contiguous_f32(base, base, const_cast<float*>(base), B, L, D);
@@ -865,7 +865,7 @@ linrec_status linrec_scan_ws(const float* a, const float* b, float* h, int64_t B
     t_last_error.clear();
     if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
     if (B == 0 || L == 0 || D == 0) return LINREC_OK;
-    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D elements overflow (B*L*D*8 must fit in 63 bits)");
     const linrec_scan_desc d = contiguous_f32(a, b, h, B, L, D);
     Problem pr;
     const linrec_status s = make_problem(&d, pr);
@@ -895,7 +895,7 @@ linrec_status linrec_scan(const float* a, const float* b, float* h, int64_t B, i
     t_last_error.clear();
     if (B < 0 || L < 0 || D < 0) return fail(LINREC_ERR_INVALID_ARGUMENT, "B, L and D must be >= 0");
     if (B == 0 || L == 0 || D == 0) return LINREC_OK;
-    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D*4 bytes overflows");
+    if (!size_ok(B, L, D)) return fail(LINREC_ERR_INVALID_ARGUMENT, "B*L*D elements overflow (B*L*D*8 must fit in 63 bits)");
     const linrec_scan_desc d = contiguous_f32(a, b, h, B, L, D);
     Problem pr;
     const linrec_status s = make_problem(&d, pr);

@@ -90,7 +90,7 @@ def test_invalid_sizes_and_null_buffers():
     assert "non-null" in binding.linrec_last_error_message()
     big = 1 << 40
     assert binding.linrec_scan_raw(64, 128, 256, big, big, 4, 0) == binding.LINREC_ERR_INVALID_ARGUMENT
-    assert "overflows" in binding.linrec_last_error_message()
+    assert "overflow" in binding.linrec_last_error_message() and "63 bits" in binding.linrec_last_error_message()
 
 
 def test_overlap_is_rejected_before_any_hip_call():
