@@ -17,7 +17,7 @@ from tests.test_parity_ex_gpu import HALF_TILES, TILES, check, say  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-CASES = 48
+CASES = 96
 DTYPES = [torch.float32, torch.bfloat16, torch.float16]
 IN_LAYOUTS = ["contiguous", "time_major", "every_other_step", "broadcast_rows"]
 
