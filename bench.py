@@ -69,7 +69,7 @@ STORAGE_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
 
 def traffic_file(workload: str, dtype: str = "f32") -> Path:
     """The counter record of a workload in a storage type, named for the kernel its plan launches."""
-    kernel = "scan_one" if current_plan(workload, dtype)["mode"] == 1 else "scan_tiles"
+    kernel = {1: "scan_one", 2: "scan_relay"}.get(current_plan(workload, dtype)["mode"], "scan_tiles")
     suffix = "" if dtype == "f32" else f"_{dtype}"
     return PROFILES / f"traffic_{kernel}_{workload}{suffix}.json"
 
@@ -173,7 +173,8 @@ def counters_by_kernel(path, counter):
             if row.get("Counter_Name") != counter:
                 continue
             name = row["Kernel_Name"]
-            key = "scan" if ("scan_tiles" in name or "scan_one" in name) else ("copy" if "copyBuffer" in name else None)
+            key = ("scan" if any(k in name for k in ("scan_tiles", "scan_one", "scan_relay"))
+                   else ("copy" if "copyBuffer" in name else None))
             if key is not None:
                 out.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)   # KiB -> bytes
     return out
@@ -533,7 +534,7 @@ def main():
         cus = torch.cuda.get_device_properties(0).multi_processor_count
         lanes = plan["lanes_per_row"]
         nseq = w.B * (w.D // (4 * lanes)) if lanes >= 8 and w.D % (4 * lanes) == 0 else 0
-        own = (args.dtype == "f32" and plan["mode"] == 0 and plan["vec"] == 4 and cus <= nseq < 2 * cus
+        own = (args.dtype == "f32" and plan["mode"] in (0, 2) and plan["vec"] == 4 and cus <= nseq < 2 * cus
                and plan["waves"] in (1, 2, 4, 8) and plan["steps_per_lane"] in (4, 8))
         if only is None and args.dtype == "f32" and (own or args.walk_shapes):
             tw = measure_tile_walk(torch, a_sets, b_sets, h_sets, (w.B, w.L, w.D), walks, stream)

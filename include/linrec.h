@@ -95,9 +95,13 @@ typedef enum linrec_status {
  * synchronisation.
  *
  * Environment: LINREC_TILE="t=<steps per lane>,w=<data waves per workgroup>,
- * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1>,l=<0|1>,x=<0|1>"
+ * vec=<1|4>,p=<lanes per row>,q=<workgroups per CU>,m=<0|1|2>,l=<0|1>,x=<0|1>"
  * overrides the tile shape, the kernel (m=0: persistent workgroups that take
- * tiles in turn; m=1: one workgroup per tile), whether persistent workgroups
+ * tiles in turn; m=1: one workgroup per tile; m=2: as m=0, except that where
+ * the carry stays local the relay kernel runs it, whose carry wave also does
+ * the scan across the lanes of each tile, one tile behind the data waves;
+ * with w > 2 or slabs wider than 64 channels, m=2 plans as m=0), whether
+ * persistent workgroups
  * may keep the carry local (l=1, the default; l=0 makes every tile look back),
  * whether channel slabs narrower than a 128-byte line are grouped so that the
  * slabs sharing a line run on one XCD (x=1, the default; x=0 keeps dispatch
@@ -123,11 +127,15 @@ typedef struct linrec_plan {
     int64_t steps_per_tile;  /* time steps one workgroup covers                        */
     int64_t chunks;          /* tiles along L for one (batch row, channel slab)        */
     int64_t tiles;           /* tiles of the problem (0 if empty); mode 1 launches one
-                                workgroup per tile, mode 0 at most as many as fit     */
+                                workgroup per tile, modes 0 and 2 at most as many as
+                                fit                                                    */
     size_t workspace_bytes;  /* device workspace the tiles need if they look back (0
                                 when chunks <= 1); unused when the carry stays local  */
     int32_t mode;            /* 0: persistent workgroups take tiles in turn;
-                                1: one workgroup per tile                              */
+                                1: one workgroup per tile;
+                                2: as 0, with the relay kernel where the carry stays
+                                local (one carry wave scans each tile's lanes, one
+                                tile behind the data waves)                            */
 } linrec_plan;
 
 /*

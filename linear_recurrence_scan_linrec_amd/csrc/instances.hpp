@@ -1,5 +1,5 @@
 // instances.hpp -- the launch table for one storage type S: every supported
-// (VEC, T, W, mode) instance of scan_tiles / scan_one, each in the plain form
+// (VEC, T, W, mode) instance of scan_tiles / scan_one / scan_relay, each in the plain form
 // and in the reverse form whose decays are one time step ahead (AHEAD), which
 // has kernels of its own so that the plain ones are not changed by it.
 // Included once per storage type by kernels_<type>.hip.
@@ -36,6 +36,19 @@ hipError_t occupancy_one(int* groups_per_cu, int threads) {
 }
 
 template <typename S, int VEC, int T, int W, bool AHEAD>
+void run_relay(dim3 grid, dim3 block, const void* a, const void* b, void* h, const linrec::Geometry& g,
+               linrec::WorkspaceHeader*, uint64_t*, hipStream_t stream) {
+    hipLaunchKernelGGL((linrec::scan_relay<S, VEC, T, W, AHEAD>), grid, block, 0, stream, static_cast<const S*>(a),
+                       static_cast<const S*>(b), static_cast<S*>(h), g);
+}
+
+template <typename S, int VEC, int T, int W, bool AHEAD>
+hipError_t occupancy_relay(int* groups_per_cu, int threads) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(groups_per_cu, linrec::scan_relay<S, VEC, T, W, AHEAD>,
+                                                        threads, 0);
+}
+
+template <typename S, int VEC, int T, int W, bool AHEAD>
 const Launch* launch_entry(int mode) {
     // register bytes a lane spends on one buffer of T positions (see tile_supported)
     constexpr int lane_bytes = VEC * T * (VEC == 4 && linrec::storage_bytes<S>() == 2 ? 2 : 4);
@@ -50,6 +63,15 @@ const Launch* launch_entry(int mode) {
         if constexpr (lane_bytes > 128) {
             return nullptr;
         } else {
+            if (mode == 2) {
+                if constexpr (W > 2) {
+                    return nullptr;
+                } else {
+                    static const Launch relay{reinterpret_cast<const void*>(&linrec::scan_relay<S, VEC, T, W, AHEAD>),
+                                              &run_relay<S, VEC, T, W, AHEAD>, &occupancy_relay<S, VEC, T, W, AHEAD>};
+                    return &relay;
+                }
+            }
             static const Launch persistent{reinterpret_cast<const void*>(&linrec::scan_tiles<S, VEC, T, W, AHEAD>),
                                            &run_tiles<S, VEC, T, W, AHEAD>, &occupancy_tiles<S, VEC, T, W, AHEAD>};
             return &persistent;

@@ -72,9 +72,16 @@ int64_t lanes_for(int p, int64_t quads) {
 //    the carry local: no status words and no cross-workgroup wait.  The widest
 //    such slab up to 32 lanes is taken (wider row segments stream better, but
 //    64-lane slabs need four carry waves and measured slower); 8 positions per
-//    lane; 2 data waves when a wave covers 8 or more row segments, else 4.
-//    (B=32 L=4096 D=256: 8-lane slabs, 76.7 us against 82.5 us looking back;
-//    B=16 L=512 D=8192: 32-lane slabs, 134 us against 146 us with 64 lanes.)
+//    lane.  Slabs of at most 64 channels go to the relay (m=2) over tiles of
+//    64 positions: the carry wave does the group scan one tile behind, and
+//    these short tiles walk memory faster than the 128-position tiles the
+//    group scan needs to stay hidden (B=32 L=4096 D=256: 72-74 us against
+//    74.5-76.5 us for 2 data waves x 128 positions with the group scan in the
+//    data waves; B=8 L=16384 D=1024: 270 against 296 us, medians).  Wider
+//    slabs keep 2 data waves when a wave covers 8 or more row segments, else
+//    4 (B=16 L=512 D=8192: 32-lane slabs, 131-134 us against 146 us with 64
+//    lanes; the relay with its 2 carry waves took 161 us there).  Looking
+//    back instead took 82.5 us at B=32 L=4096 D=256.
 //  - Otherwise the tiles look back: persistent workgroups of 8 data waves, 4
 //    positions per lane and 32 lanes (512 bytes of fp32) per row segment; with
 //    fewer than 32 sequences each chain is long, and one workgroup per tile
@@ -122,6 +129,15 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         const int64_t nseq = B * ((quads + lanes - 1) / lanes);
         bool local = false;
         for (int m = 1; m <= linrec::kMaxLocalSeqs && !local; ++m) local = nseq % m == 0 && nseq / m >= cus;
+        // the relay when its grid is one workgroup per CU (with 8 positions
+        // per lane and 4 channels it fills a SIMD's registers, so one per
+        // CU is all that is resident): tiles of 64 positions, 1 data wave for
+        // 8-lane slabs, 2 for 16-lane ones
+        if (local && lanes * vec <= 64 && nseq % cus == 0 && nseq / cus <= linrec::kMaxLocalSeqs) {
+            const int64_t groups = 64 / lanes;
+            const int w = groups >= 8 ? 1 : 2;
+            if (L > w * groups * 8) return TileShape{vec, 8, w, p, 0, 2, 1};
+        }
         const int w = 64 / lanes >= 8 ? 2 : 4;
         const int64_t steps = static_cast<int64_t>(w) * (64 / lanes) * 8;
         if (local && L > steps) return TileShape{vec, 8, w, p, 0, 0, 1};
@@ -176,9 +192,9 @@ bool apply_tile_env(TileShape& s, int es, std::string& err) {
     }
     if (!tile_supported(s, es)) {
         err = "LINREC_TILE asks for an unsupported tile (t in {4,8,16}, w in {1,2,4,7,8,15}, vec in {1,4}, "
-              "p a power of two <= 64, q in [0, 64], m in {0,1}, l in {0,1}, x in {0,1}; with r register bytes per "
-              "channel and position (2 for 16-bit storage with vec=4, else 4): vec*t*r <= 128 for m=0 and "
-              "<= 64 for w=15)";
+              "p a power of two <= 64, q in [0, 64], m in {0,1,2}, l in {0,1}, x in {0,1}; with r register bytes "
+              "per channel and position (2 for 16-bit storage with vec=4, else 4): vec*t*r <= 128 for m=0 and m=2 "
+              "and <= 64 for w=15)";
         return false;
     }
     return true;
@@ -330,6 +346,9 @@ linrec_status make_plan(const Problem& pr, Plan& p, int cus) {
     g.groups = linrec::kWave / lanes;
     g.slab_channels = lanes * s.vec;
     g.carry_waves = (g.slab_channels + linrec::kWave - 1) / linrec::kWave;
+    // the relay has one carry wave and at most 2 data waves; other shapes of
+    // m=2 run as m=0
+    if (s.m == 2 && (s.w > 2 || g.carry_waves > 1)) s.m = p.tile.m = 0;
     if ((s.w + g.carry_waves) * linrec::kWave > 1024)
         return fail(LINREC_ERR_INVALID_ARGUMENT, "the tile needs more than 1024 threads per workgroup (data waves w "
                                                  "plus one carry wave per 64 slab channels); pick a smaller w or p");
@@ -699,13 +718,22 @@ linrec_status run_scan(const Problem& pr, void* stream, const WorkspaceSource& s
     if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
     const int threads = (p.tile.w + p.geom.carry_waves) * linrec::kWave;
     int64_t groups = p.tiles;   // one tile per workgroup
-    if (p.tile.m == 0) {
+    if (p.tile.m != 1) {
         // persistent workgroups: a grid that gives each of them whole
         // sequences when there is one (the carry then stays local), else as
         // many as fit at once (or q per CU), never more than there are tiles
         int64_t resident = 0;
         if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
         groups = local_grid(p, resident, cus);
+        if (groups == 0 && p.tile.m == 2) {
+            // no local carry: the relay needs one, so the tiles look back
+            // through the m=0 kernel of the same shape
+            TileShape looked = p.tile;
+            looked.m = 0;
+            fn = pick_launch(q.dtype, looked, ahead);
+            if (fn == nullptr) return fail(LINREC_ERR_INVALID_ARGUMENT, "no kernel for the chosen tile");
+            if ((s = resident_groups(device, fn, threads, resident)) != LINREC_OK) return s;
+        }
         if (groups == 0) {
             groups = resident;
             if (p.tile.q > 0) groups = std::min<int64_t>(resident, static_cast<int64_t>(p.tile.q) * cus);

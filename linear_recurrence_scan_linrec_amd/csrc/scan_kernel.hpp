@@ -433,12 +433,9 @@ __device__ __forceinline__ TileIndex tile_index(const Geometry& g, int64_t tile)
 }
 
 template <typename S>
-__device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const Geometry& g, int64_t tile,
-                                           int wave, int quad, int grp, int vec, int T) {
+__device__ __forceinline__ TileSpot locate_at(const S* a, const S* b, S* h, const Geometry& g, const TileIndex& ix,
+                                              int wave, int quad, int grp, int vec, int T) {
     TileSpot s;
-    // the chunk is the slow index: a tile's predecessors come before it in
-    // every workgroup's order, and the tiles in flight spread over all sequences
-    const TileIndex ix = tile_index<S>(g, tile);
     s.chunk = ix.chunk;
     s.seq = ix.seq;
     s.row = ix.row;
@@ -457,6 +454,14 @@ __device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const G
     s.b = operand_spot<S>(b, g.b_sb, g.b_sl, g, s.row, t_lo, span, rel, d0, s.d_ok);
     s.h = operand_spot<S>(h, g.h_sb, g.h_sl, g, s.row, t_lo, span, rel, d0, s.d_ok);
     return s;
+}
+
+template <typename S>
+__device__ __forceinline__ TileSpot locate(const S* a, const S* b, S* h, const Geometry& g, int64_t tile,
+                                           int wave, int quad, int grp, int vec, int T) {
+    // the chunk is the slow index: a tile's predecessors come before it in
+    // every workgroup's order, and the tiles in flight spread over all sequences
+    return locate_at<S>(a, b, h, g, tile_index<S>(g, tile), wave, quad, grp, vec, T);
 }
 
 // (1) loads of one tile into a register buffer.  Positions past L and channels
@@ -878,6 +883,334 @@ struct LocalCarry {
     double h[kMaxLocalSeqs][kWave * VEC];
 };
 
+// ---------------------------------------------------------------------------
+// Relay: persistent workgroups whose carry stays local, with the group scan
+// moved from the data waves to the carry wave and the carry one tile behind.
+//
+// A workgroup whose tiles are chunks 0, 1, ... of its own local_seqs = m
+// sequences (tile k of the workgroup: chunk k / m of its sequence k mod m)
+// needs no status words.  Each data-wave lane composes its own T positions
+// into one pair and puts it into LDS; the carry wave folds the W * G pairs of
+// each slab channel in the order of their positions, in fp64, from the state
+// entering the tile, and writes back, in place of each lane's B, the state
+// entering that lane's positions (rounded to fp32 once).  In step k the data
+// waves put tile k's pairs into LDS slot k & 1, pass one barrier, then replay
+// tile k-1 from the states that the carry wave wrote into slot (k-1) & 1
+// during step k-1; after the same barrier the carry wave turns tile k's pairs
+// into its entering states.  One barrier per tile, and neither a group scan
+// nor the carry sits on the data waves' path.  Their register buffers rotate
+// through four tiles: the one whose pairs are formed, the one replayed, and
+// two whose loads are in flight.  The tiles' positions advance by counting, so
+// no division by the sequence count sits in the loop.
+struct LocalPos {
+    int64_t chunk;
+    int j;   // which of the workgroup's sequences
+};
+
+__device__ __forceinline__ LocalPos advance(LocalPos p, int m) {
+    return p.j + 1 == m ? LocalPos{p.chunk + 1, 0} : LocalPos{p.chunk, p.j + 1};
+}
+
+// The decomposition of the workgroup's tile at position p: with one sequence
+// per workgroup it never changes (s0); otherwise the slot's sequence, batch
+// row and slab are recomputed (32-bit: there are fewer than 2^31 tiles).
+struct LocalSeqs {
+    TileIndex s0;
+};
+
+template <typename S>
+__device__ __forceinline__ TileIndex local_index(const Geometry& g, const LocalSeqs& ls, LocalPos p) {
+    if (g.local_seqs == 1) {
+        TileIndex r = ls.s0;
+        r.chunk = p.chunk;
+        return r;
+    }
+    const uint32_t slot = static_cast<uint32_t>(blockIdx.x) + static_cast<uint32_t>(p.j) * gridDim.x;
+    const uint32_t seq = static_cast<uint32_t>(sequence_of(g, slot));
+    const uint32_t nslab = static_cast<uint32_t>(g.nslab);
+    const uint32_t row = seq / nslab;
+    return TileIndex{p.chunk, seq, row, seq - row * nslab};
+}
+
+template <typename S>
+__device__ __forceinline__ LocalSeqs local_sequences(const Geometry& g) {
+    return LocalSeqs{tile_index<S>(g, blockIdx.x)};
+}
+
+// The spots of one local-carry sequence's full tiles differ only in where
+// each operand's descriptor starts: chunk c's start lies c * delta bytes after
+// chunk 0's (before it, in reverse: delta < 0); offsets, steps and ranges are
+// the same.  A ragged last chunk is located in full.  With one sequence per
+// workgroup this replaces each tile's 64-bit offset arithmetic by one scalar
+// multiply-add per operand.
+struct SeqWalk {
+    TileSpot s0;                        // chunk 0
+    const char *a0, *b0, *h0;           // chunk 0's descriptor bases
+    int64_t da, db, dh;                 // their advance per chunk, in bytes
+    int nrec_a, nrec_b, nrec_h;         // range of a full tile
+    int64_t ragged;                     // chunk located in full (nchunks when none)
+};
+
+template <typename S>
+__device__ __forceinline__ SeqWalk seq_walk(const S* a, const S* b, S* h, const Geometry& g, const TileIndex& ix0,
+                                            int wave, int quad, int grp, int vec, int T) {
+    SeqWalk w;
+    TileIndex i0 = ix0;
+    i0.chunk = 0;
+    w.s0 = locate_at<S>(a, b, h, g, i0, wave, quad, grp, vec, T);
+    constexpr int64_t es = storage_bytes<S>();
+    const int64_t steps = g.steps_per_tile;
+    const int64_t dir = g.reverse ? -1 : 1;
+    // chunk 0's range starts at time step 0 (forward) or L - steps (reverse) of the batch row
+    const int64_t t0 = g.reverse ? g.L - steps : 0;
+    w.a0 = reinterpret_cast<const char*>(a + w.s0.row * g.a_sb + t0 * g.a_sl);
+    w.b0 = reinterpret_cast<const char*>(b + w.s0.row * g.b_sb + t0 * g.b_sl);
+    w.h0 = reinterpret_cast<const char*>(h + w.s0.row * g.h_sb + t0 * g.h_sl);
+    w.da = dir * steps * g.a_sl * es;
+    w.db = dir * steps * g.b_sl * es;
+    w.dh = dir * steps * g.h_sl * es;
+    auto nrec = [&](int64_t sl) {
+        const int64_t bytes = ((steps - 1) * sl + g.D) * es;
+        return static_cast<int>(bytes < kMaxRange ? bytes : kMaxRange);
+    };
+    w.nrec_a = nrec(g.a_sl);
+    w.nrec_b = nrec(g.b_sl);
+    w.nrec_h = nrec(g.h_sl);
+    w.ragged = g.L % steps != 0 ? g.nchunks - 1 : g.nchunks;
+    return w;
+}
+
+template <typename S>
+__device__ __forceinline__ TileSpot walk_spot(const S* a, const S* b, S* h, const Geometry& g, const SeqWalk& w,
+                                              const TileIndex& ix0, int64_t chunk, int wave, int quad, int grp,
+                                              int vec, int T) {
+    if (chunk == w.ragged) {
+        TileIndex i = ix0;
+        i.chunk = chunk;
+        return locate_at<S>(a, b, h, g, i, wave, quad, grp, vec, T);
+    }
+    TileSpot s = w.s0;
+    s.chunk = chunk;
+    s.tau0 = w.s0.tau0 + chunk * g.steps_per_tile;
+    s.a.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(w.a0 + chunk * w.da), 0, w.nrec_a, kBufferConfig);
+    s.b.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(w.b0 + chunk * w.db), 0, w.nrec_b, kBufferConfig);
+    s.h.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(w.h0 + chunk * w.dh), 0, w.nrec_h, kBufferConfig);
+    return s;
+}
+
+// The spot of the workgroup's tile at position p.
+template <typename S>
+__device__ __forceinline__ TileSpot local_spot(const S* a, const S* b, S* h, const Geometry& g, const LocalSeqs& ix,
+                                               const SeqWalk& w, LocalPos p, int wave, int quad, int grp, int vec,
+                                               int T) {
+    if (g.local_seqs == 1) return walk_spot<S>(a, b, h, g, w, ix.s0, p.chunk, wave, quad, grp, vec, T);
+    return locate_at<S>(a, b, h, g, local_index<S>(g, ix, p), wave, quad, grp, vec, T);
+}
+
+// (2) of the relay: a lane's pair of its T positions, into LDS at
+// [wave][lane] (lane = group * P + quad).  Without h_init the state before
+// position 0 is zero, so that position's a never contributes: use 0 for it
+// (1 in the form with the decays ahead, where h_init enters with decay 1).
+// With h_final, positions past L become identity steps (see scan_registers).
+template <typename S, int VEC, int T, int W, bool AHEAD>
+__device__ __forceinline__ void lane_pair(const Geometry& g, TileShared<VEC, W>& sh, const TileSpot& s, int lane,
+                                          int wave, Reg<S, VEC> (&av)[T], Reg<S, VEC> (&bv)[T]) {
+    if (s.tau0 == 0 && g.h_init == nullptr) set_reg<S, VEC>(av[0], 0.0f);
+    else if (AHEAD && s.tau0 == 0) set_reg<S, VEC>(av[0], 1.0f);
+    if (g.h_final != nullptr && (s.chunk + 1) * g.steps_per_tile > g.L) {
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+            if (s.tau0 + j >= g.L) {
+                set_reg<S, VEC>(av[j], 1.0f);
+                set_reg<S, VEC>(bv[j], 0.0f);
+            }
+        }
+    }
+    Vec<VEC> in_b = widen<S, VEC>(bv[0]);
+#pragma unroll
+    for (int j = 1; j < T; ++j) {
+        const Vec<VEC> aj = widen<S, VEC>(av[j]), bj = widen<S, VEC>(bv[j]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) in_b.v[i] = __builtin_fmaf(aj.v[i], in_b.v[i], bj.v[i]);
+    }
+    VecD<VEC> in_a;
+    {
+        Vec<VEC> aw[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) aw[j] = widen<S, VEC>(av[j]);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) in_a.v[i] = decay_product<0, T>(aw, i);
+    }
+    sh.pair_a[wave][lane] = in_a;
+    sh.pair_b[wave][lane] = in_b;
+}
+
+// (6) of the relay: replay from the state entering the lane's positions,
+// which the carry wave left at [wave][lane].  Stores past L or D are dropped.
+template <typename S, int VEC, int T, int W>
+__device__ __forceinline__ void replay_lane(const Geometry& g, const TileShared<VEC, W>& sh, const TileSpot& s,
+                                            int wave, int lane, int quad, const Reg<S, VEC> (&av)[T],
+                                            const Reg<S, VEC> (&bv)[T]) {
+    LanePrefix<VEC> none;
+    none.ex_a = splat<VEC>(1.0f);
+    none.ex_b = splat<VEC>(0.0f);
+    replay_from<S, VEC, T>(g, sh.pair_b[wave][lane], s, quad, none, av, bv);
+}
+
+// One step of the relay's data waves: loads of tile k+2 into (la, lb) (past
+// the workgroup's last tile every offset is out of range), the pairs of tile
+// k (loaded two steps earlier, in (sa, sb)) into LDS slot k & 1, the barrier,
+// the replay of tile k-1 (in (ra, rb)).  In step 0 the replay runs with every
+// store out of range, so that every step issues the same memory operations
+// and the compiler's waits for each tile's loads stay exact.
+template <typename S, int VEC, int T, int W, bool AHEAD>
+__device__ __forceinline__ void relay_step(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
+                                           const Geometry& g, TileShared<VEC, W> (&sh)[2], const LocalSeqs& ix,
+                                           const SeqWalk& sw, int lane, int wave, int quad, int grp, int64_t k,
+                                           int64_t n, LocalPos pk, Reg<S, VEC> (&sa)[T], Reg<S, VEC> (&sb)[T],
+                                           const Reg<S, VEC> (&ra)[T], const Reg<S, VEC> (&rb)[T],
+                                           Reg<S, VEC> (&la)[T], Reg<S, VEC> (&lb)[T]) {
+    const int m = g.local_seqs;
+    {
+        const LocalPos p2 = advance(advance(pk, m), m);
+        TileSpot ns = local_spot<S>(a, b, h, g, ix, sw, k + 2 < n ? p2 : pk, wave, quad, grp, VEC, T);
+        if (k + 2 >= n) ns.a.off = ns.b.off = kOutOfRange;
+        load_tile<S, VEC, T, AHEAD>(la, lb, ns);
+    }
+    const TileSpot s = local_spot<S>(a, b, h, g, ix, sw, pk, wave, quad, grp, VEC, T);
+    lane_pair<S, VEC, T, W, AHEAD>(g, sh[k & 1], s, lane, wave, sa, sb);
+    __syncthreads();   // tile k's pairs are in slot k & 1; tile k-1's entering states in the other
+    const bool have_prev = k >= 1;
+    const LocalPos pp = LocalPos{pk.j == 0 ? pk.chunk - 1 : pk.chunk, pk.j == 0 ? m - 1 : pk.j - 1};
+    TileSpot rs = local_spot<S>(a, b, h, g, ix, sw, have_prev ? pp : pk, wave, quad, grp, VEC, T);
+    if (!have_prev) {
+        rs.h.off = kOutOfRange;
+        rs.d_ok = false;   // no final-state store either
+    }
+    replay_lane<S, VEC, T, W>(g, sh[(k - 1) & 1], rs, wave, lane, quad, ra, rb);
+}
+
+// A replay whose stores are all out of range (nothing is written): issues the
+// memory operations of one replay.
+template <typename S, int VEC, int T, int W>
+__device__ __forceinline__ void idle_replay(const Geometry& g, const TileShared<VEC, W>& sh, TileSpot s, int wave,
+                                            int lane, int quad, const Reg<S, VEC> (&ra)[T],
+                                            const Reg<S, VEC> (&rb)[T]) {
+    s.h.off = kOutOfRange;
+    s.d_ok = false;
+    replay_lane<S, VEC, T, W>(g, sh, s, wave, lane, quad, ra, rb);
+}
+
+// The relay's data waves.  Four register buffers rotate: step k forms the
+// pairs of buffer k % 4, replays buffer (k-1) % 4 and loads tile k+2 into
+// buffer (k+2) % 4 (which held tile k-2).  A local carry has at least two
+// chunks per sequence, so every workgroup has n >= 2 tiles.
+template <typename S, int VEC, int T, int W, bool AHEAD>
+__device__ __forceinline__ void relay_data_waves(const S* __restrict__ a, const S* __restrict__ b,
+                                                 S* __restrict__ h, const Geometry& g, TileShared<VEC, W> (&sh)[2],
+                                                 int lane, int wave, int quad, int grp) {
+    const int m = g.local_seqs;
+    const int64_t n = g.nchunks * m;
+    const LocalSeqs ix = local_sequences<S>(g);
+    const SeqWalk sw = seq_walk<S>(a, b, h, g, ix.s0, wave, quad, grp, VEC, T);
+    Reg<S, VEC> a0[T], b0[T], a1[T], b1[T], a2[T], b2[T], a3[T], b3[T];
+    LocalPos pk{0, 0};
+    {
+        // the loop is entered with what every step leaves in flight: a tile's
+        // loads, a replay's stores, the next tile's loads, a replay's stores
+        const TileSpot s0 = local_spot<S>(a, b, h, g, ix, sw, pk, wave, quad, grp, VEC, T);
+        load_tile<S, VEC, T, AHEAD>(a0, b0, s0);
+        idle_replay<S, VEC, T, W>(g, sh[1], s0, wave, lane, quad, a3, b3);
+        const TileSpot s1 = local_spot<S>(a, b, h, g, ix, sw, advance(pk, m), wave, quad, grp, VEC, T);
+        load_tile<S, VEC, T, AHEAD>(a1, b1, s1);
+        idle_replay<S, VEC, T, W>(g, sh[1], s0, wave, lane, quad, a3, b3);
+    }
+    int64_t k = 0;
+    for (;;) {
+        relay_step<S, VEC, T, W, AHEAD>(a, b, h, g, sh, ix, sw, lane, wave, quad, grp, k, n, pk, a0, b0, a3, b3, a2, b2);
+        pk = advance(pk, m);
+        if (++k >= n) break;
+        relay_step<S, VEC, T, W, AHEAD>(a, b, h, g, sh, ix, sw, lane, wave, quad, grp, k, n, pk, a1, b1, a0, b0, a3, b3);
+        pk = advance(pk, m);
+        if (++k >= n) break;
+        relay_step<S, VEC, T, W, AHEAD>(a, b, h, g, sh, ix, sw, lane, wave, quad, grp, k, n, pk, a2, b2, a1, b1, a0, b0);
+        pk = advance(pk, m);
+        if (++k >= n) break;
+        relay_step<S, VEC, T, W, AHEAD>(a, b, h, g, sh, ix, sw, lane, wave, quad, grp, k, n, pk, a3, b3, a2, b2, a1, b1);
+        pk = advance(pk, m);
+        if (++k >= n) break;
+    }
+    __syncthreads();   // the last tile's entering states are in slot (n-1) & 1
+    // replay of tile n-1, whose buffer is the one the last step formed
+    const LocalPos pl = LocalPos{pk.j == 0 ? pk.chunk - 1 : pk.chunk, pk.j == 0 ? m - 1 : pk.j - 1};
+    const TileSpot rs = local_spot<S>(a, b, h, g, ix, sw, pl, wave, quad, grp, VEC, T);
+    TileShared<VEC, W>& last_slot = sh[(n - 1) & 1];
+    const int last = static_cast<int>((n - 1) & 3);
+    if (last == 0) replay_lane<S, VEC, T, W>(g, last_slot, rs, wave, lane, quad, a0, b0);
+    else if (last == 1) replay_lane<S, VEC, T, W>(g, last_slot, rs, wave, lane, quad, a1, b1);
+    else if (last == 2) replay_lane<S, VEC, T, W>(g, last_slot, rs, wave, lane, quad, a2, b2);
+    else replay_lane<S, VEC, T, W>(g, last_slot, rs, wave, lane, quad, a3, b3);
+}
+
+// (5) of the relay, for slab channel c (c < slab_channels <= 64: one carry
+// wave): fold the tile's lane pairs in the order of their positions, from the
+// state entering the tile (h_init or zero for chunk 0, else this channel's
+// local cell), replacing each lane's B by the state entering that lane's
+// positions; the state after the tile goes back into the local cell.  The
+// pairs are read in batches of 8 so that their LDS latency is paid once per
+// batch, not once per pair.
+template <int VEC, int W>
+__device__ __forceinline__ void relay_carry(const Geometry& g, TileShared<VEC, W>& sh, int c, const TileIndex& ix,
+                                            double* local) {
+    if (c >= g.slab_channels) return;
+    const int64_t d = ix.slab * g.slab_channels + c;
+    double hv = 0.0;
+    if (d < g.D) hv = ix.chunk == 0 ? initial_state(g, ix.row, d) : *local;
+    const double* pa = &sh.pair_a[0][0].v[0];
+    float* pb = &sh.pair_b[0][0].v[0];
+    const int G = g.groups, P = g.lanes_d;
+    constexpr int kBatch = 8;
+#pragma unroll
+    for (int v = 0; v < W; ++v) {
+        for (int g0 = 0; g0 < G; g0 += kBatch) {
+            double ra[kBatch];
+            float rb[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int gr = g0 + j < G ? g0 + j : G - 1;
+                const int k = (v * kWave + gr * P) * VEC + c;
+                ra[j] = pa[k];
+                rb[j] = pb[k];
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                if (g0 + j < G) {
+                    const int k = (v * kWave + (g0 + j) * P) * VEC + c;
+                    pb[k] = static_cast<float>(hv);
+                    hv = __builtin_fma(ra[j], hv, static_cast<double>(rb[j]));
+                }
+            }
+        }
+    }
+    *local = hv;
+}
+
+template <typename S, int VEC, int W>
+__device__ __forceinline__ void relay_carry_wave(const Geometry& g, TileShared<VEC, W> (&sh)[2],
+                                                 LocalCarry<VEC>& local, int c) {
+    const int m = g.local_seqs;
+    const int64_t n = g.nchunks * m;
+    const LocalSeqs ix = local_sequences<S>(g);
+    LocalPos pk{0, 0};
+    for (int64_t k = 0; k < n; ++k) {
+        const TileIndex t = local_index<S>(g, ix, pk);
+        __syncthreads();   // tile k's pairs are in slot k & 1
+        relay_carry<VEC, W>(g, sh[k & 1], c, t, &local.h[pk.j][c]);
+        pk = advance(pk, m);
+    }
+    __syncthreads();   // pairs with the data waves' last barrier
+}
+
 // Data wave, one tile of the persistent loop: start the loads of the
 // workgroup's next tile into (nav, nbv), scan the tile whose inputs are in
 // (av, bv), hand the wave's pair to the carry wave, and once the carry is in,
@@ -987,6 +1320,25 @@ scan_tiles(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h,
         data_tile<S, VEC, T, W, AHEAD>(a, b, h, g, sh, lane, wave, quad, grp, tile, a0, b0, tile + stride, a1, b1);
         tile += stride;
     }
+}
+
+// Relay workgroup: W data waves and one carry wave (slabs of at most 64
+// channels), launched only with a grid that keeps the carry local
+// (g.local_seqs > 0, g.nchunks > 1): workgroup k takes sequences k, k + grid,
+// ... (through sequence_of), chunk by chunk.
+template <typename S, int VEC, int T, int W, bool AHEAD>
+__global__ void __launch_bounds__((W + 1) * kWave)
+scan_relay(const S* __restrict__ a, const S* __restrict__ b, S* __restrict__ h, Geometry g) {
+    __shared__ TileShared<VEC, W> sh[2];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (wave >= W) {
+        __shared__ LocalCarry<VEC> local;
+        relay_carry_wave<S, VEC, W>(g, sh, local, lane);
+        return;
+    }
+    relay_data_waves<S, VEC, T, W, AHEAD>(a, b, h, g, sh, lane, wave, lane & (g.lanes_d - 1),
+                                          lane >> g.log2_lanes_d);
 }
 
 // One tile per workgroup (grid = number of tiles) of W data waves and

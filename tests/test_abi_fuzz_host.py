@@ -111,7 +111,7 @@ def test_random_descriptors_follow_the_documented_rules():
             assert plan.chunks == -(-d.L // plan.steps_per_tile), label
             assert plan.tiles % plan.chunks == 0, label
             assert (plan.workspace_bytes > 0) == (plan.chunks > 1), label
-            assert plan.vec in (1, 4) and plan.mode in (0, 1), label
+            assert plan.vec in (1, 4) and plan.mode in (0, 1, 2), label
     # the draw exercises every branch
     assert min(counts.values()) > 20, counts
 

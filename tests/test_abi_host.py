@@ -164,7 +164,16 @@ def test_tile_override(tile_env):
         binding.linrec_scan_plan(32, 4096, 256)
     os.environ["LINREC_TILE"] = "w=15,p=16,t=4"
     assert binding.linrec_scan_plan(32, 4096, 256)["waves"] == 15
-    for bad in ("t=5", "w=3", "w=16", "w=5", "vec=2", "t=16", "m=3", "m=2,w=2", "m=2,t=8,w=8", "w=14,t=8", "m=-1", "m=0,vec=4,t=16", "x=2", "t", "t=abc", "p=3", "p=128", "p=0",
+    # the relay (m=2): at most 2 data waves and one carry wave, else the plan runs as m=0
+    os.environ["LINREC_TILE"] = "m=2,t=4,w=2"
+    p = binding.linrec_scan_plan(32, 4096, 256)
+    assert (p["mode"], p["steps_per_lane"], p["waves"], p["lanes_per_row"]) == (2, 4, 2, 8)
+    for demoted in ("m=2,w=4", "m=2,t=8,w=8", "w=4", "p=32"):   # the last two on the default m=2
+        os.environ["LINREC_TILE"] = demoted
+        assert binding.linrec_scan_plan(32, 4096, 256)["mode"] == 0, demoted
+    os.environ["LINREC_TILE"] = "m=2,vec=1,p=64,t=8,w=1"   # 64 channels: one carry wave
+    assert binding.linrec_scan_plan(32, 4096, 256)["mode"] == 2
+    for bad in ("t=5", "w=3", "w=16", "w=5", "vec=2", "t=16", "m=3", "m=2,vec=4,t=16", "w=14,t=8", "m=-1", "m=0,vec=4,t=16", "x=2", "t", "t=abc", "p=3", "p=128", "p=0",
                 "q=-1", "q=65", "d=1"):
         os.environ["LINREC_TILE"] = bad
         with pytest.raises(binding.LinrecError) as err:
@@ -276,9 +285,9 @@ def test_ex_empty_problems_without_a_final_state_are_noops():
 # assume), as measured and chosen: a change to the rules shows up here first.
 DEFAULT_PLANS = {
     # (B, L, D, dtype): (vec, steps_per_lane, waves, lanes_per_row, mode)
-    (32, 4096, 256, 0): (4, 8, 2, 8, 0),        # fp32 pages shape: local carry over 128-byte rows
+    (32, 4096, 256, 0): (4, 8, 1, 8, 2),        # fp32 pages shape: the relay over 128-byte rows, 64-step tiles
     (16, 512, 8192, 0): (4, 8, 4, 32, 0),       # wide_channels: local carry, 4 sequences per workgroup
-    (8, 16384, 1024, 0): (4, 8, 2, 8, 0),       # near_unit_resets: local carry
+    (8, 16384, 1024, 0): (4, 8, 1, 8, 2),       # near_unit_resets: the relay
     (2, 262144, 64, 0): (4, 8, 7, 8, 1),        # long_sequence: one tile per workgroup, two per CU
     (32, 4096, 256, 1): (4, 16, 7, 16, 1),      # bf16 pages shape: one tile per workgroup (1280 tiles)
     (16, 512, 8192, 1): (4, 8, 8, 64, 0),       # bf16 wide_channels: local carry over 64-lane slabs

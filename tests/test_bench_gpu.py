@@ -38,9 +38,9 @@ def test_bench_prints_one_json_line_with_roofline_and_oracle_baseline(monkeypatc
     assert ceil["contiguous"]["rows"] == 1 and ceil["scan_order"]["rows"] == 32
     assert r["ceiling_gbs"] == ceil["contiguous"]["gbs"] > 0
     assert r["frac_of_ceiling"] == pytest.approx(roof["achieved"] / r["ceiling_gbs"], abs=1e-3)
-    # the same stream in the plan's own tile walk (8-lane slabs, 2 waves, 8 rows per lane)
+    # the same stream in the plan's own tile walk (8-lane slabs, 1 wave, 8 rows per lane)
     tw = ceil["tile_walk"]
-    assert (tw["lanes"], tw["waves"], tw["steps_per_lane"]) == (8, 2, 8) and tw["gbs"] > 0
+    assert (tw["lanes"], tw["waves"], tw["steps_per_lane"]) == (8, 1, 8) and tw["gbs"] > 0
     assert tw["frac_scan"] == pytest.approx(roof["achieved"] / tw["gbs"], abs=1e-3)
     single = r["single_launch_us"]
     assert single["cold"]["n"] == 2 and single["warm"]["n"] == 2 and single["cold"]["mean"] > 0

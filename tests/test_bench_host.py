@@ -28,13 +28,15 @@ def test_counters_by_kernel_keeps_scan_and_copy_rows_in_bytes(tmp_path):
         [4, "some_other_kernel", "FETCH_SIZE", 5.0],    # another kernel: ignored
         [5, SCAN, "FETCH_SIZE", 300.0],
         [6, "void linrec::scan_one<float, 4, 4, 15>(float const*, ...)", "FETCH_SIZE", 50.0],
+        [7, "void linrec::scan_relay<float, 4, 8, 1>(float const*, ...)", "FETCH_SIZE", 60.0],
     ])
     got = bench.counters_by_kernel(path, "FETCH_SIZE")
-    assert got == {"scan": [100.0 * 1024, 300.0 * 1024, 50.0 * 1024], "copy": [262144.0 * 1024]}
+    assert got == {"scan": [100.0 * 1024, 300.0 * 1024, 50.0 * 1024, 60.0 * 1024], "copy": [262144.0 * 1024]}
 
 
 def test_traffic_file_is_named_for_the_planned_kernel():
-    assert bench.traffic_file("pages_shape").name == "traffic_scan_tiles_pages_shape.json"
+    assert bench.traffic_file("pages_shape").name == "traffic_scan_relay_pages_shape.json"
+    assert bench.traffic_file("wide_channels").name == "traffic_scan_tiles_wide_channels.json"
     assert bench.traffic_file("long_sequence").name == "traffic_scan_one_long_sequence.json"
     assert bench.traffic_file("pages_shape", "bf16").name == "traffic_scan_one_pages_shape_bf16.json"
     assert bench.traffic_file("near_unit_resets", "f16").name == "traffic_scan_tiles_near_unit_resets_f16.json"
