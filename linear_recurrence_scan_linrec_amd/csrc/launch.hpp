@@ -34,10 +34,9 @@ inline int register_bytes(int vec, int storage_bytes) { return vec == 4 && stora
 
 // Instantiated tile shapes, for a storage type of storage_bytes per element.
 // Persistent workgroups keep two register buffers of T positions x VEC
-// channels, which spill beyond 128 bytes a lane each (the relay keeps four,
-// which at 128 bytes fill the 256 VGPRs and put a few values in AGPRs); 15
-// data waves leave at most 128 registers a lane, which spill beyond 64 bytes
-// of positions.
+// channels, which spill beyond 128 bytes a lane each (the relay keeps three);
+// 15 data waves leave at most 128 registers a lane, which spill beyond 64
+// bytes of positions.
 inline bool tile_supported(const TileShape& s, int storage_bytes = 4) {
     const bool vec_ok = s.vec == 1 || s.vec == 4;
     const bool t_ok = s.t == 4 || s.t == 8 || s.t == 16;

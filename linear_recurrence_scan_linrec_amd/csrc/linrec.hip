@@ -129,10 +129,9 @@ TileShape default_tile(int64_t B, int64_t L, int64_t D, bool vec4, int cus, int 
         const int64_t nseq = B * ((quads + lanes - 1) / lanes);
         bool local = false;
         for (int m = 1; m <= linrec::kMaxLocalSeqs && !local; ++m) local = nseq % m == 0 && nseq / m >= cus;
-        // the relay when its grid is one workgroup per CU (with 8 positions
-        // per lane and 4 channels it fills a SIMD's registers, so one per
-        // CU is all that is resident): tiles of 64 positions, 1 data wave for
-        // 8-lane slabs, 2 for 16-lane ones
+        // the relay when the sequences come to 1 to 4 per CU, so that its
+        // grid is one workgroup per CU, the grid it was measured with: tiles
+        // of 64 positions, 1 data wave for 8-lane slabs, 2 for 16-lane ones
         if (local && lanes * vec <= 64 && nseq % cus == 0 && nseq / cus <= linrec::kMaxLocalSeqs) {
             const int64_t groups = 64 / lanes;
             const int w = groups >= 8 ? 1 : 2;
