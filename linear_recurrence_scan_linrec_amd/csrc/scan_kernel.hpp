@@ -1116,6 +1116,13 @@ __device__ __forceinline__ void relay_data_waves(const S* __restrict__ a, const 
     const LocalSeqs ix = local_sequences<S>(g);
     const SeqWalk sw = seq_walk<S>(a, b, h, g, ix.s0, wave, quad, grp, VEC, T);
     Reg<S, VEC> a0[T], b0[T], a1[T], b1[T], a2[T], b2[T];
+    // the replays before the first tile's (preamble and step 0) read buffer 2
+    // and store nothing; give them defined values
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+        set_reg<S, VEC>(a2[j], 0.0f);
+        set_reg<S, VEC>(b2[j], 0.0f);
+    }
     LocalPos pk{0, 0};
     {
         // the loop is entered with what every step leaves in flight: a tile's
